@@ -1,0 +1,170 @@
+/*
+ * spec_verify -- batched verification of drafted tokens on one AMD Instinct
+ * MI355X (gfx950).  C ABI; plain pointers and sizes only.
+ *
+ * The operation (one verification step for B sequences at once):
+ *   A draft model proposes K tokens per sequence; the target model scores the
+ *   whole block in one pass; the verifier keeps the longest prefix the target
+ *   accepts and appends one token the target generates itself; everything after
+ *   the first rejection is discarded.
+ *     - umans.ai blog "DeepSeek V4 Pro DSpark: the model isn't ready, the
+ *       architecture is", section "Speculative decoding, briefly";
+ *     - zhichai.net article on DSpark, section "Why LLMs speak so slowly"
+ *       (generation restarts from the first error).
+ *   Acceptance is rejection sampling on the target/draft probability ratio so
+ *   that emitted tokens follow the target distribution exactly (same two
+ *   sections).  Concretely, with p = softmax(target_logits / T) and
+ *   q = softmax(draft_logits / T) at position j:
+ *     accept x_j  iff  u_j < p_j(x_j) / q_j(x_j)      (probability min(1, p/q));
+ *     after the first rejection at j*, the replacement is drawn from
+ *     max(0, p_j* - q_j*) normalised, by inverse CDF in ascending token id;
+ *     when every verified position is accepted, the bonus token is drawn from
+ *     p of the next row by inverse CDF.
+ *   T == 0 selects greedy verification: the target token is the argmax of the
+ *   raw target row (lowest id on ties); x_j is accepted iff it equals it.
+ *
+ *   Verify length (confidence scheduling): each draft position carries a
+ *   confidence c_j, the probability that it survives given that all earlier
+ *   positions survived; the survival of a prefix is the product along the
+ *   block; how many positions to verify depends on these survivals and the
+ *   load.
+ *     - umans.ai blog, section "2. Verify smarter: a throttle that costs the
+ *       user nothing"; zhichai.net article, section "Under the hood".
+ *   This library's rule:  S_0 = 1,  S_j = S_{j-1} * c_j,
+ *                         L = max({0} U {j in 1..K : S_j >= tau}),
+ *   with tau given per sequence (the load-dependent threshold) and c either
+ *   given by the caller or c_j = max_v q_j(v).  Only positions 1..L are tested.
+ *
+ * Layout (all device memory, row-major, vocabulary contiguous):
+ *   target_logits  element (b, j, v), j = 0..K (row K is the bonus row),
+ *                  at target_logits + b*target_batch_stride + j*target_row_stride + v
+ *   draft_logits   element (b, j, v), j = 0..K-1, same scheme with draft strides
+ *   both tensors share one element type (SV_F32 or SV_BF16, set at create).
+ *   Strides are in elements; a batch stride of 0 shares one set of rows among
+ *   all sequences.  Row strides must be >= V.
+ *   draft_tokens   int32 [B][K]
+ *   uniforms       float [B][K+1]: column j < K is the accept test of position
+ *                  j+1; column K is the final (replacement or bonus) draw.
+ *                  Values in (0, 1).
+ *
+ * Outputs (device, caller-allocated):
+ *   accepted_len   int32 [B]      a_b, number of accepted drafted tokens
+ *   out_tokens     int32 [B][K+1] x_1..x_a, then the final token, then -1
+ *   verify_len_out int32 [B]      L_b
+ *   optional (NULL = skip; entries the step does not evaluate are left untouched):
+ *   lse_target     float [B][K+1] log-sum-exp of target_logits/T for rows 1..a+1
+ *   lse_draft      float [B][K]   same for the draft rows the step reads
+ *   survival       float [B][K]   S_j (tau mode; with derived c, for the
+ *                                 positions whose draft row was read)
+ *   residual_mass  float [B]      Z = sum max(0, p - q) of the replacement draw;
+ *                                 1 for a bonus draw; 0 if a rejection met Z <= 0
+ *                                 (then the draw falls back to p); NaN for greedy
+ *   sampled_prob   float [B]      probability of the final token under its draw
+ *   device_status  int32 [1]      0, or SV_STATUS_* bits (see below)
+ *
+ * Ownership: the caller owns every buffer and keeps it alive until the work
+ * queued on the stream has finished.  The handle owns its workspace, allocated
+ * once by spec_verify_create; spec_verify_run allocates nothing.
+ *
+ * Streams and threads: spec_verify_run only enqueues work on the given HIP
+ * stream (NULL = the default stream) and never synchronises the host.  One
+ * handle serves one stream at a time; calls that overlap on one handle race.
+ * Separate handles are independent.
+ *
+ * Errors: argument checks run on the host before anything is enqueued and
+ * return SV_EINVAL / SV_EUNSUPPORTED with outputs untouched.  A failed launch
+ * returns SV_EDEVICE.  Drafted ids outside [0, V) at a tested position, or a
+ * given verify length outside [0, K], are found on the device: that sequence
+ * gets a = 0 and no token (-1), and SV_STATUS_BAD_INPUT is set.
+ *
+ * Determinism: for identical inputs the outputs are bitwise identical from run
+ * to run, and a sequence's outputs do not depend on its batch position or on B.
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct spec_verify spec_verify_t; /* opaque handle */
+
+enum { SV_OK = 0, SV_EINVAL = -1, SV_ENOMEM = -2, SV_EDEVICE = -3, SV_EUNSUPPORTED = -4 };
+enum { SV_F32 = 0, SV_BF16 = 1 };
+enum { SV_LEN_FIXED = 0, SV_LEN_TAU = 1 };
+enum { SV_STATUS_BAD_INPUT = 1, SV_STATUS_TIMEOUT = 2 };
+
+/* Limits checked by spec_verify_create. */
+#define SV_MAX_VOCAB 1048576
+#define SV_MAX_BATCH 1048575
+#define SV_MAX_DRAFT 1000
+
+typedef struct {
+    int32_t max_batch; /* 1..SV_MAX_BATCH; workspace is sized from these three */
+    int32_t max_draft; /* 1..SV_MAX_DRAFT */
+    int32_t vocab;     /* V, 1..SV_MAX_VOCAB */
+    int32_t dtype;     /* SV_F32 | SV_BF16, for both logit tensors */
+    int32_t device;    /* HIP device ordinal */
+} spec_verify_config;
+
+typedef struct {
+    int32_t B, K;                  /* 0 <= B <= max_batch; 1 <= K <= max_draft */
+    const void* target_logits;     /* see layout above */
+    int64_t target_batch_stride, target_row_stride;
+    const void* draft_logits;      /* NULL allowed iff temperature == 0 */
+    int64_t draft_batch_stride, draft_row_stride;
+    const int32_t* draft_tokens;   /* [B][K] */
+    const float* uniforms;         /* [B][K+1]; NULL allowed iff temperature == 0 */
+    float temperature;             /* > 0 rejection sampling; == 0 greedy */
+    int32_t length_mode;           /* SV_LEN_FIXED | SV_LEN_TAU */
+    const int32_t* verify_len_in;  /* FIXED: [B] in [0, K], or NULL => L = K */
+    const float* confidence;       /* TAU: [B][K] in [0, 1], or NULL => c_j = max_v q_j(v) (needs T > 0) */
+    const float* tau;              /* TAU: [B] */
+    int32_t* accepted_len;         /* [B] */
+    int32_t* out_tokens;           /* [B][K+1] */
+    int32_t* verify_len_out;       /* [B] */
+    float* lse_target;             /* optional [B][K+1] */
+    float* lse_draft;              /* optional [B][K] */
+    float* survival;               /* optional [B][K] */
+    float* residual_mass;          /* optional [B] */
+    float* sampled_prob;           /* optional [B] */
+    int32_t* device_status;        /* optional [1] */
+} spec_verify_args;
+
+/* Allocate a handle and its workspace on cfg->device.  *out is set only on SV_OK. */
+int spec_verify_create(const spec_verify_config* cfg, spec_verify_t** out);
+
+/* Host-only argument check of one call against a configuration; touches no
+ * device state.  Returns SV_OK, SV_EINVAL or SV_EUNSUPPORTED. */
+int spec_verify_check(const spec_verify_config* cfg, const spec_verify_args* a);
+
+/* Enqueue one verification step on hip_stream (a hipStream_t, or NULL). */
+int spec_verify_run(spec_verify_t* h, const spec_verify_args* a, void* hip_stream);
+
+/* Free the handle.  The caller synchronises the stream first.  NULL is a no-op. */
+int spec_verify_destroy(spec_verify_t* h);
+
+/* Static description of a status code. */
+const char* spec_verify_status_string(int status);
+
+/* Per-kernel timing with HIP events, for benchmarks.  After
+ * spec_verify_timing_begin(h, max_calls), the next max_calls runs record an
+ * event before and after each kernel on the run's stream.
+ * spec_verify_timing_end synchronises those events, writes the summed
+ * milliseconds of kernel k to ms[k] (k < n_kernels, see
+ * spec_verify_kernel_name), the number of timed runs to *n_runs, and frees
+ * the events. */
+int spec_verify_timing_begin(spec_verify_t* h, int32_t max_calls);
+int spec_verify_timing_end(spec_verify_t* h, double* ms, int32_t n_kernels, int32_t* n_runs);
+
+/* Number of kernels a run launches, and the name of kernel k (static string). */
+int32_t spec_verify_kernel_count(void);
+const char* spec_verify_kernel_name(int32_t k);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_VERIFY_H */

@@ -1,0 +1,390 @@
+/*
+ * CPU ORACLE for batched draft verification -- TEST INFRASTRUCTURE ONLY.
+ *
+ * Only the test suite, the smoke check and the benchmark's CPU-baseline leg
+ * may load this library.  The product path (the HIP library) never calls it and
+ * shares no code, header, table or helper with it.
+ *
+ * It is the plain definition of one verification step, in fp64, one sequence
+ * at a time, in the order the pages describe it:
+ *
+ *  - The draft proposes a block; the target scores the whole block in one pass;
+ *    the prefix the target agrees with is kept, plus one token the target
+ *    generates itself; the rest is discarded.
+ *      (umans.ai blog "DeepSeek V4 Pro DSpark: the model isn't ready, the
+ *       architecture is", section "Speculative decoding, briefly";
+ *       zhichai.net article, section "Why LLMs speak so slowly": generation
+ *       restarts from the first error.)
+ *  - The acceptance rule is rejection sampling on the ratio of target to draft
+ *    probability, built so that the emitted tokens follow the target's
+ *    distribution exactly; a rejected token is replaced by one the target
+ *    would have produced.
+ *      (umans.ai blog, "Speculative decoding, briefly"; zhichai.net, "Why LLMs
+ *       speak so slowly".)  The construction that meets this statement is the
+ *    standard one: accept x with probability min(1, p(x)/q(x)); on rejection
+ *    draw the replacement from max(0, p - q) normalised.
+ *  - A confidence per draft position is the probability that the token
+ *    survives given that everything before it survived; multiplying along the
+ *    block gives the survival of each prefix; the verify length follows from
+ *    these survivals and the load.
+ *      (umans.ai blog, section "2. Verify smarter: a throttle that costs the
+ *       user nothing"; zhichai.net, section "Under the hood".)  The rule used
+ *    here: S_0 = 1, S_j = S_{j-1} c_j, L = max({0} U {j : S_j >= tau}).
+ *
+ * Readings where the pages are silent (each is listed in the design notes):
+ *  - K+1 target rows per sequence; row K+1 is the distribution of the bonus
+ *    token after the whole block.
+ *  - One temperature T for target and draft: p = softmax(l_t / T),
+ *    q = softmax(l_d / T).  T == 0 means greedy: target token = argmax of the
+ *    raw target row (lowest index on ties), accept while the draft equals it.
+ *  - Uniforms u[b][0..K-1] serve the accept tests of positions 1..K; u[b][K]
+ *    serves the final draw (replacement or bonus).  Accept iff u < p/q.
+ *  - Inverse CDF in ascending token id: y = min{v : C_v > w}, C the running
+ *    sum.  If rounding leaves w >= C_{V-1}, y = the largest v with mass > 0.
+ *    If the residual mass Z is not positive, the replacement is drawn from p.
+ *  - c_j = max_v q_j(v) when no confidence is given.
+ *  - A drafted id outside [0, V) at a position that is tested, or a given
+ *    verify length outside [0, K], marks the sequence bad: accepted length 0,
+ *    no token (-1).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { SVO_F32 = 0, SVO_BF16 = 1 };
+enum { SVO_LEN_FIXED = 0, SVO_LEN_TAU = 1 };
+enum { SVO_FINAL_RESIDUAL = 0, SVO_FINAL_BONUS = 1, SVO_FINAL_GREEDY = 2, SVO_FINAL_BAD_INPUT = 3 };
+enum { SVO_MARGIN_ACCEPT = 1, SVO_MARGIN_CDF = 2, SVO_MARGIN_SURVIVAL = 4 };
+
+#define SVO_MARGIN 1e-6
+
+typedef struct {
+    int32_t B, K, V;
+    int32_t dtype;
+    const void* target;              /* [B][K+1][V] via the strides below (elements) */
+    int64_t target_batch_stride, target_row_stride;
+    const void* draft;               /* [B][K][V]; NULL allowed when T == 0 */
+    int64_t draft_batch_stride, draft_row_stride;
+    const int32_t* tokens;           /* [B][K] */
+    const float* uniforms;           /* [B][K+1] */
+    float temperature;
+    int32_t length_mode;
+    const int32_t* verify_len_in;    /* fixed mode: [B] or NULL (=> K) */
+    const float* confidence;         /* tau mode: [B][K] or NULL (=> max draft prob) */
+    const float* tau;                /* tau mode: [B] */
+    const int32_t* seq_index;        /* sequences to evaluate, or NULL => 0..n_seq-1 */
+    int32_t n_seq;
+    int32_t all_rows;                /* 1: report lse of every row, not only the rows the step reads */
+    int32_t n_threads;               /* <= 0: library default */
+} svo_problem;
+
+typedef struct {                     /* indexed by i in 0..n_seq-1 */
+    int32_t* accepted_len;           /* [n] */
+    int32_t* out_tokens;             /* [n][K+1], -1 padded */
+    int32_t* verify_len;             /* [n] */
+    double* lse_target;              /* [n][K+1], NaN where not evaluated */
+    double* lse_draft;               /* [n][K],   NaN where not evaluated */
+    double* survival;                /* [n][K],   NaN where not evaluated */
+    double* residual_mass;           /* [n] Z of the replacement draw, 1 for a bonus draw */
+    double* sampled_prob;            /* [n] probability of the final token under its draw */
+    int32_t* final_kind;             /* [n] SVO_FINAL_* */
+    int32_t* margin;                 /* [n] SVO_MARGIN_* bits */
+    double* accept_gap;              /* [n] min |u_j - ratio_j| over tested positions (inf if none) */
+    double* cdf_gap;                 /* [n] normalised distance of w to the nearest CDF step (inf if greedy) */
+    int32_t* alt_token;              /* [n] the token across the nearest CDF step, -1 if none */
+} svo_result;
+
+/* Element v of a row as fp64 (bf16 is the upper half of an fp32 pattern). */
+static inline double load_logit(const void* base, int dtype, int64_t idx)
+{
+    if (dtype == SVO_BF16) {
+        uint32_t bits = (uint32_t)((const uint16_t*)base)[idx] << 16;
+        float f;
+        memcpy(&f, &bits, 4);
+        return (double)f;
+    }
+    return (double)((const float*)base)[idx];
+}
+
+/* log-sum-exp of z = l / T over one row: lse = m + ln sum exp(z - m). */
+static double row_lse(const void* base, int dtype, int64_t off, int32_t V, double T)
+{
+    double m = -INFINITY;
+    for (int32_t v = 0; v < V; ++v) {
+        double z = load_logit(base, dtype, off + v) / T;
+        if (z > m) m = z;
+    }
+    double s = 0.0;
+    for (int32_t v = 0; v < V; ++v) s += exp(load_logit(base, dtype, off + v) / T - m);
+    return m + log(s);
+}
+
+/* max_v softmax(l/T)_v of one row. */
+static double row_max_prob(const void* base, int dtype, int64_t off, int32_t V, double T, double lse)
+{
+    double m = -INFINITY;
+    for (int32_t v = 0; v < V; ++v) {
+        double z = load_logit(base, dtype, off + v) / T;
+        if (z > m) m = z;
+    }
+    return exp(m - lse);
+}
+
+/* Argmax of the raw row, lowest index on ties. */
+static int32_t row_argmax(const void* base, int dtype, int64_t off, int32_t V)
+{
+    int32_t best = 0;
+    double bv = load_logit(base, dtype, off);
+    for (int32_t v = 1; v < V; ++v) {
+        double x = load_logit(base, dtype, off + v);
+        if (x > bv) { bv = x; best = v; }
+    }
+    return best;
+}
+
+/* Inverse-CDF draw over masses r[0..V-1] in ascending id: y = min{v : C_v > w}
+ * with C the running sum.  If no step passes w (rounding), y = the largest v
+ * with r_v > 0.  *gap = distance of w to the nearest of C_{y-1}, C_y divided by
+ * norm; *alt = the token across that step (-1 if none). */
+static int32_t inverse_cdf(const double* r, int32_t V, double w, double norm, double* gap, int32_t* alt)
+{
+    double C = 0.0, C_prev = 0.0;
+    int32_t y = -1, prev_pos = -1;
+    for (int32_t v = 0; v < V; ++v) {
+        C_prev = C;
+        C += r[v];
+        if (C > w) { y = v; break; }
+        if (r[v] > 0.0) prev_pos = v;
+    }
+    if (y < 0) {
+        for (int32_t v = V - 1; v >= 0; --v)
+            if (r[v] > 0.0) { y = v; break; }
+        *gap = 0.0;
+        *alt = -1;
+        return y;
+    }
+    const double below = fabs(w - C_prev), above = fabs(C - w);
+    if (below <= above) {
+        *gap = below / norm;
+        *alt = prev_pos;
+    } else {
+        *gap = above / norm;
+        *alt = -1;
+        for (int32_t v = y + 1; v < V; ++v)
+            if (r[v] > 0.0) { *alt = v; break; }
+    }
+    return y;
+}
+
+static void verify_one(const svo_problem* P, int32_t b, int32_t i, const svo_result* R, double* r)
+{
+    const int32_t K = P->K, V = P->V;
+    const double T = (double)P->temperature;
+    const int greedy = !(T > 0.0);
+    const int64_t tb = (int64_t)b * P->target_batch_stride;
+    const int64_t db = (int64_t)b * P->draft_batch_stride;
+    const int32_t* x = P->tokens + (int64_t)b * K;
+    const float* u = P->uniforms ? P->uniforms + (int64_t)b * (K + 1) : NULL;
+    int32_t* out = R->out_tokens + (int64_t)i * (K + 1);
+    double* lse_t = R->lse_target + (int64_t)i * (K + 1);
+    double* lse_d = R->lse_draft + (int64_t)i * K;
+    double* surv = R->survival + (int64_t)i * K;
+
+    for (int32_t j = 0; j <= K; ++j) { out[j] = -1; lse_t[j] = NAN; }
+    for (int32_t j = 0; j < K; ++j) { lse_d[j] = NAN; surv[j] = NAN; }
+    int32_t margin = 0;
+    double accept_gap = INFINITY, cdf_gap = INFINITY;
+    int32_t alt = -1;
+
+    /* ---- verify length ---- */
+    int32_t L;
+    if (P->length_mode == SVO_LEN_FIXED) {
+        L = P->verify_len_in ? P->verify_len_in[b] : K;
+        if (L < 0 || L > K) {
+            /* outside the block: the sequence is marked bad, nothing is emitted */
+            R->accepted_len[i] = 0;
+            R->verify_len[i] = L;
+            R->residual_mass[i] = NAN;
+            R->sampled_prob[i] = NAN;
+            R->final_kind[i] = SVO_FINAL_BAD_INPUT;
+            R->margin[i] = 0;
+            R->accept_gap[i] = INFINITY;
+            R->cdf_gap[i] = INFINITY;
+            R->alt_token[i] = -1;
+            return;
+        }
+    } else {
+        const double tau = (double)P->tau[b];
+        double S = 1.0;
+        L = 0;
+        for (int32_t j = 1; j <= K; ++j) {
+            double c;
+            if (P->confidence) {
+                c = (double)P->confidence[(int64_t)b * K + (j - 1)];
+            } else {
+                const int64_t off = db + (int64_t)(j - 1) * P->draft_row_stride;
+                lse_d[j - 1] = row_lse(P->draft, P->dtype, off, V, T);
+                c = row_max_prob(P->draft, P->dtype, off, V, T, lse_d[j - 1]);
+            }
+            S *= c;
+            surv[j - 1] = S;
+            if (S >= tau) L = j;
+        }
+        /* margin on the survivals the step has to look at */
+        for (int32_t j = 1; j <= K && j <= L + 1; ++j) {
+            double scale = tau > 1e-30 ? tau : 1e-30;
+            if (fabs(surv[j - 1] - tau) < SVO_MARGIN * scale) margin |= SVO_MARGIN_SURVIVAL;
+        }
+    }
+
+    int32_t a = 0, y = -1, kind;
+    double Z = 1.0, py = NAN;
+
+    if (greedy) {
+        /* ---- greedy: accept while the drafted id equals the target argmax ---- */
+        kind = SVO_FINAL_GREEDY;
+        int bad = 0;
+        for (int32_t j = 1; j <= L; ++j) {
+            if (x[j - 1] < 0 || x[j - 1] >= V) { bad = 1; break; }
+            const int32_t g = row_argmax(P->target, P->dtype, tb + (int64_t)(j - 1) * P->target_row_stride, V);
+            if (x[j - 1] != g) break;
+            a = j;
+        }
+        if (bad) {
+            kind = SVO_FINAL_BAD_INPUT; a = 0; y = -1;
+        } else {
+            y = row_argmax(P->target, P->dtype, tb + (int64_t)a * P->target_row_stride, V);
+        }
+    } else {
+        /* ---- rejection sampling along the block, stop at the first rejection ---- */
+        int bad = 0, rejected = 0;
+        for (int32_t j = 1; j <= L; ++j) {
+            const int64_t toff = tb + (int64_t)(j - 1) * P->target_row_stride;
+            const int64_t doff = db + (int64_t)(j - 1) * P->draft_row_stride;
+            if (isnan(lse_t[j - 1])) lse_t[j - 1] = row_lse(P->target, P->dtype, toff, V, T);
+            if (isnan(lse_d[j - 1])) lse_d[j - 1] = row_lse(P->draft, P->dtype, doff, V, T);
+            const int32_t xj = x[j - 1];
+            if (xj < 0 || xj >= V) { bad = 1; break; }
+            const double p = exp(load_logit(P->target, P->dtype, toff + xj) / T - lse_t[j - 1]);
+            const double q = exp(load_logit(P->draft, P->dtype, doff + xj) / T - lse_d[j - 1]);
+            const double ratio = q > 0.0 ? p / q : INFINITY;
+            const double uj = (double)u[j - 1];
+            const double gap = fabs(uj - ratio);
+            if (gap < accept_gap) accept_gap = gap;
+            if (gap < SVO_MARGIN) margin |= SVO_MARGIN_ACCEPT;
+            if (uj < ratio) {
+                a = j;
+            } else {
+                rejected = 1;
+                break;
+            }
+        }
+        if (bad) {
+            kind = SVO_FINAL_BAD_INPUT; a = 0; y = -1; Z = 1.0;
+        } else {
+            const int32_t js = a + 1; /* the row of the final draw (1-based) */
+            const int64_t toff = tb + (int64_t)(js - 1) * P->target_row_stride;
+            if (isnan(lse_t[js - 1])) lse_t[js - 1] = row_lse(P->target, P->dtype, toff, V, T);
+            const double uf = (double)u[K];
+            int use_p = !rejected;
+            if (rejected) {
+                /* replacement from max(0, p - q), normalised: w = u * Z */
+                const int64_t doff = db + (int64_t)(js - 1) * P->draft_row_stride;
+                double Zr = 0.0;
+                for (int32_t v = 0; v < V; ++v) {
+                    const double p = exp(load_logit(P->target, P->dtype, toff + v) / T - lse_t[js - 1]);
+                    const double q = exp(load_logit(P->draft, P->dtype, doff + v) / T - lse_d[js - 1]);
+                    r[v] = p > q ? p - q : 0.0;
+                    Zr += r[v];
+                }
+                kind = SVO_FINAL_RESIDUAL;
+                if (Zr > 0.0) {
+                    y = inverse_cdf(r, V, uf * Zr, Zr, &cdf_gap, &alt);
+                    Z = Zr;
+                    py = r[y] / Zr;
+                } else {
+                    use_p = 1; /* cannot happen in exact arithmetic after a rejection */
+                    Z = 0.0;
+                }
+            } else {
+                kind = SVO_FINAL_BONUS;
+                Z = 1.0;
+            }
+            if (use_p) {
+                /* bonus (or the degenerate replacement): draw from p of that row, w = u */
+                for (int32_t v = 0; v < V; ++v)
+                    r[v] = exp(load_logit(P->target, P->dtype, toff + v) / T - lse_t[js - 1]);
+                y = inverse_cdf(r, V, uf, 1.0, &cdf_gap, &alt);
+                py = r[y];
+            }
+            if (cdf_gap < SVO_MARGIN) margin |= SVO_MARGIN_CDF;
+        }
+    }
+
+    if (P->all_rows && !greedy) {
+        for (int32_t j = 1; j <= K + 1; ++j)
+            if (isnan(lse_t[j - 1]))
+                lse_t[j - 1] = row_lse(P->target, P->dtype, tb + (int64_t)(j - 1) * P->target_row_stride, V, T);
+        if (P->draft)
+            for (int32_t j = 1; j <= K; ++j)
+                if (isnan(lse_d[j - 1]))
+                    lse_d[j - 1] = row_lse(P->draft, P->dtype, db + (int64_t)(j - 1) * P->draft_row_stride, V, T);
+    }
+
+    /* ---- emit: accepted prefix, then the final token ---- */
+    if (y >= 0) {
+        for (int32_t j = 0; j < a; ++j) out[j] = x[j];
+        out[a] = y;
+    }
+    R->accepted_len[i] = a;
+    R->verify_len[i] = L;
+    R->residual_mass[i] = greedy ? NAN : Z;
+    R->sampled_prob[i] = py;
+    R->final_kind[i] = kind;
+    R->margin[i] = margin;
+    R->accept_gap[i] = accept_gap;
+    R->cdf_gap[i] = cdf_gap;
+    R->alt_token[i] = alt;
+}
+
+/* Returns 0, or -1 for arguments the definition does not cover. */
+int svo_verify(const svo_problem* P, const svo_result* R)
+{
+    if (!P || !R || P->B < 0 || P->K < 1 || P->V < 1 || P->n_seq < 0) return -1;
+    const int greedy = !(P->temperature > 0.0f);
+    if (!greedy && (!P->draft || !P->uniforms)) return -1;
+    if (P->length_mode == SVO_LEN_TAU && !P->tau) return -1;
+    if (P->length_mode == SVO_LEN_TAU && greedy && !P->confidence) return -1;
+    if (P->temperature < 0.0f || isnan(P->temperature)) return -1;
+#ifdef _OPENMP
+    if (P->n_threads > 0) omp_set_num_threads(P->n_threads);
+#endif
+    int err = 0;
+    #pragma omp parallel reduction(| : err)
+    {
+        double* r = (double*)malloc(sizeof(double) * (size_t)P->V);
+        if (!r) err = 1;
+        #pragma omp for schedule(dynamic, 4)
+        for (int32_t i = 0; i < P->n_seq; ++i) {
+            if (!r) continue;
+            const int32_t b = P->seq_index ? P->seq_index[i] : i;
+            verify_one(P, b, i, R, r);
+        }
+        free(r);
+    }
+    return err ? -1 : 0;
+}
+
+int svo_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
