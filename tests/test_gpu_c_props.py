@@ -1,0 +1,99 @@
+"""GPU properties: bitwise determinism, batch invariance, and the emitted
+distribution (chi-square) on many sequences sharing one set of rows."""
+import numpy as np
+import pytest
+from scipy import special, stats
+
+from oracle import oracle as O
+from synth import synth
+from tests import parity_util as PU
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _D():
+    from draft_verification_amd import device as D
+    return D
+
+
+def test_bitwise_determinism():
+    D = _D()
+    w = synth.WORKLOADS["zipf64"].with_(B=32)
+    prob = synth.make_problem(w)
+    print("[case] determinism zipf B32", flush=True)
+    dp = D.from_problem(prob)
+    sv = D.handle_for(dp)
+    outs = []
+    for _ in range(5):
+        sv.run(dp.args())
+        outs.append(dp.fetch())
+    sv.close()
+    for o in outs[1:]:
+        for k, v in o.items():
+            if v is not None:
+                assert np.array_equal(v.view(np.uint8), outs[0][k].view(np.uint8)), k
+
+
+@pytest.mark.parametrize("name", ["zipf64", "peaked512"])
+def test_batch_invariance(name):
+    D = _D()
+    w = synth.WORKLOADS[name].with_(B=48, V=40000)
+    prob = synth.make_problem(w)
+    print(f"[case] batch invariance {name}", flush=True)
+    full = D.run_once(D.from_problem(prob))
+    sel = np.array([47, 3, 3, 20, 0, 11, 29], np.int64)
+    sub = synth.Problem(w.with_(B=len(sel)), np.ascontiguousarray(prob.target[sel]),
+                        np.ascontiguousarray(prob.draft[sel]), np.ascontiguousarray(prob.tokens[sel]),
+                        np.ascontiguousarray(prob.uniforms[sel]), None,
+                        None if prob.tau is None else np.ascontiguousarray(prob.tau[sel]))
+    part = D.run_once(D.from_problem(sub))
+    for k, v in part.items():
+        if v is None or k == "device_status":
+            continue
+        assert np.array_equal(v.view(np.uint8), full[k][sel].view(np.uint8)), k
+
+
+def _shared_rows(seed, K, V, T):
+    rng = np.random.default_rng(seed)
+    t = (1.0 * rng.standard_normal((K + 1, V))).astype(np.float32)
+    d = (t[:K] + 0.7 * rng.standard_normal((K, V))).astype(np.float32)
+    q = special.softmax(d.astype(np.float64) / np.float64(np.float32(T)), axis=1)
+    p = special.softmax(t.astype(np.float64) / np.float64(np.float32(T)), axis=1)
+    return t, d, p, q
+
+
+@pytest.mark.parametrize("mode", ["fixed", "tau"])
+def test_chi_square_shared_rows(mode):
+    # 2e5 sequences verify the same rows (batch stride 0) with fresh draft samples
+    # and uniforms: the emitted token at each position follows p_j, and every
+    # sequence matches the oracle exactly outside the margin.
+    D = _D()
+    K, V, N, T = 4, 8, 200000, 0.9
+    t, d, p, q = _shared_rows(50, K, V, T)
+    toks = np.stack([synth.uniforms(600 + j, N) for j in range(K)], axis=1)
+    for j in range(K):
+        c = np.cumsum(q[j]); c[-1] = 1.0
+        toks[:, j] = np.searchsorted(c, toks[:, j], side="right")
+    toks = toks.astype(np.int32)
+    u = synth.uniforms(700, N * (K + 1)).reshape(N, K + 1)
+    if mode == "tau":
+        S = np.cumprod(q.max(axis=1))
+        tau = np.full(N, np.float32(S[2] * 0.999), np.float32)
+        L = 3
+        dp = D.DeviceProblem.upload(t, d, toks, u, T, D.F32, length_mode=1, tau=tau)
+    else:
+        tau, L = None, K
+        dp = D.DeviceProblem.upload(t, d, toks, u, T, D.F32)
+    print(f"[case] chi-square {mode} N={N}", flush=True)
+    res = D.run_once(dp)
+    orc = O.verify(t, d, toks, u, T, dtype=O.F32, length_mode=1 if tau is not None else 0, tau=tau)
+    rep = PU.compare(f"chi2 {mode}", res, orc, dtype=O.F32, derived=tau is not None)
+    print(rep.line(), flush=True)
+    assert not rep.mismatches, rep.mismatches[:5]
+    for j in range(L + 1):
+        sel = res["accepted_len"] >= j
+        counts = np.bincount(res["out_tokens"][sel, j], minlength=V)
+        pv = stats.chisquare(counts, p[j] * sel.sum()).pvalue
+        assert pv > 1e-4, (j, pv)
