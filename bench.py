@@ -1,0 +1,244 @@
+#!/usr/bin/env python3
+"""Benchmark of one batched verification step on one MI355X.
+
+Workload (the block the confidence-scheduled configuration describes, with
+every drafted position verified): B = 256 sequences, K = 16 drafted positions,
+V = 129280, bf16 target and draft logits (target 2*N(0,1), draft = target +
+N(0, sigma_j) with sigma_j rising 0.3 -> 1.5 along the block), T = 1,
+confidence c_j = max draft probability, tau = 0 for every sequence, so
+L_b = 16.  Inputs are synthetic, seeded, and resident in HBM before timing;
+two input sets alternate between steps.
+
+Printed: one JSON line with the metric (verified draft positions per second),
+the step time, the roofline of the dominant kernel (HBM bound) and the CPU
+oracle timed on this host as a baseline.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+    python bench.py --copy-calibration     # plain 1 GiB copy, for counter scaling
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "verified draft positions/sec and achieved HBM GB/s at V=129280 (1 MI355X)"
+PEAK_HBM_GBPS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_sv_rows_B256_K16_V129280_bf16_tau0.json")
+KERNEL_SRC = os.path.join(ROOT, "draft_verification_amd", "csrc", "spec_verify.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def workload(seed_shift=0):
+    from synth import synth
+    return synth.WORKLOADS["sched256"].with_(tau_choices=(0.0,), seed=3 + seed_shift)
+
+
+def step_bytes(res, w) -> dict:
+    """Algorithmic bytes of one step: every logit row the step streams, once.
+
+    Rows are walked in position groups, so a sequence streams the target and
+    draft rows of every group up to the one holding its first rejection (or its
+    bonus row); rows inside that group past the rejection are within the verify
+    window and are counted like the others.  The per-sequence count comes from
+    the library (rows_read).  Per-position inputs (token, uniform) and outputs
+    are added; re-reads for the final draw are not counted."""
+    es = 2 if w.dtype == 1 else 4
+    a = res["accepted_len"].astype(np.int64)
+    L = res["verify_len_out"].astype(np.int64)
+    K, V = w.K, w.V
+    rows = int(res["rows_read"].astype(np.int64).sum())
+    tested = np.minimum(a + 1, L)
+    io = int((tested * 8 + 4).sum() + w.B * ((K + 1) * 4 + 8))
+    needed_rows = int((a + 1).sum() + np.minimum(a + 1, L).sum())   # up to the first rejection only
+    window_rows = int(((L + 1) + np.minimum(L + 1, K)).sum())       # every row up to L+1
+    return dict(bytes=rows * V * es + io, rows=rows, needed_bytes=needed_rows * V * es + io,
+                window_bytes=window_rows * V * es + io, per_row_bytes=V * es)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    with open(KERNEL_SRC, "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_entry(src_hash: str):
+    """HBM bytes per launch from committed counter runs, if they match this source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_src_sha") != src_hash:
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(prob, L_total, seconds=10.0, max_reps=8):
+    from oracle import oracle as O
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    threads = max(1, min(threads, len(os.sched_getaffinity(0))))
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        O.verify_problem(prob, threads=threads)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or reps >= max_reps:
+            break
+    cpu_model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"value": reps * L_total / el, "unit": "verified draft positions/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"the full step ({prob.w.B} sequences, {L_total} verified positions) run {reps} times "
+                      f"in {el:.2f} s on the host CPU ({cpu_model})"}
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    reps = 10
+    for _ in range(reps):
+        dst.copy_(src)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / reps
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "ms": ms, "gbps_rw": 2 * n / ms / 1e6}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this benchmark runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(the verification step has no cross-GPU part; see the design notes on sharding).",
+              file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    import torch
+    from draft_verification_amd import binding as B
+    from draft_verification_amd import device as D
+    from synth import synth
+
+    t0 = time.perf_counter()
+    probs = [synth.make_problem(workload(s)) for s in (0, 1000)]
+    log(f"[bench] inputs generated in {time.perf_counter() - t0:.1f} s")
+    w = probs[0].w
+    dps = [D.from_problem(p, diagnostics=False) for p in probs]
+    sv = B.SpecVerify(w.B, w.K, w.V, w.dtype, 0)
+    stream = torch.cuda.current_stream().cuda_stream
+    argv = [dp.args() for dp in dps]
+
+    for i in range(args.warmup):
+        sv.run(argv[i % 2], stream)
+    torch.cuda.synchronize()
+    outs = [dp.fetch() for dp in dps]
+    for o in outs:
+        assert o["device_status"][0] == 0, "device reported bad input or a timeout"
+
+    # whole-step timing (no per-kernel events)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for i in range(args.steps):
+        sv.run(argv[i % 2], stream)
+    ev1.record()
+    torch.cuda.synchronize()
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+
+    # per-kernel timing (HIP events around each launch, same stream)
+    sv.timing_begin(args.steps)
+    for i in range(args.steps):
+        sv.run(argv[i % 2], stream)
+    torch.cuda.synchronize()
+    kms, nruns = sv.timing_end()
+    kernel_avg_ms = {k: v / max(nruns, 1) for k, v in kms.items()}
+    sv.close()
+
+    L_total = [int(o["verify_len_out"].sum()) for o in outs]
+    acc = [step_bytes(o, w) for o in outs]
+    bytes_step = sum(a["bytes"] for a in acc) / 2.0
+    window_step = sum(a["window_bytes"] for a in acc) / 2.0
+    needed_step = sum(a["needed_bytes"] for a in acc) / 2.0
+    positions = sum(L_total) / 2.0
+    value = positions / (ms_step / 1e3)
+    dom = "sv_rows"
+    dom_ms = kernel_avg_ms[dom]
+    achieved = bytes_step / (dom_ms / 1e3) / 1e9
+    src_hash = kernel_source_hash()
+    traffic = traffic_entry(src_hash)
+    mean_a = float(np.mean([o["accepted_len"].mean() for o in outs]))
+
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "verified draft positions/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded generator; no dataset)",
+        "config": {"workload": "confidence-scheduled verify, every position verified: B=256 K=16 V=129280 "
+                               "bf16 logits, T=1, c=max draft prob, tau=0 (L=16)",
+                   "B": w.B, "K": w.K, "V": w.V, "logits": "bf16", "temperature": w.temperature, "tau": 0.0,
+                   "input_sets": 2},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic, "kernel": dom,
+                     "kernel_avg_ms": dom_ms, "algorithmic_bytes_per_launch": bytes_step},
+        "step_hbm_gbps": bytes_step / (ms_step / 1e3) / 1e9,
+        "emitted_tokens_per_s": float(np.mean([o["accepted_len"].sum() + w.B for o in outs])) / (ms_step / 1e3),
+        "mean_accepted": mean_a,
+        "window_bytes_per_step": window_step,
+        "first_rejection_bytes_per_step": needed_step,
+        "rows_per_step": sum(a["rows"] for a in acc) / 2.0,
+        "kernel_avg_ms": kernel_avg_ms,
+        "kernel_src_sha": src_hash,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on the same workload ...")
+        out["cpu_baseline"] = cpu_baseline(probs[0], L_total[0])
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

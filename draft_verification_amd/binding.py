@@ -43,7 +43,8 @@ class Args(ctypes.Structure):
         ("verify_len_in", ctypes.c_void_p), ("confidence", ctypes.c_void_p), ("tau", ctypes.c_void_p),
         ("accepted_len", ctypes.c_void_p), ("out_tokens", ctypes.c_void_p), ("verify_len_out", ctypes.c_void_p),
         ("lse_target", ctypes.c_void_p), ("lse_draft", ctypes.c_void_p), ("survival", ctypes.c_void_p),
-        ("residual_mass", ctypes.c_void_p), ("sampled_prob", ctypes.c_void_p), ("device_status", ctypes.c_void_p),
+        ("residual_mass", ctypes.c_void_p), ("sampled_prob", ctypes.c_void_p), ("rows_read", ctypes.c_void_p),
+        ("device_status", ctypes.c_void_p),
     ]
 
 
@@ -108,7 +109,7 @@ def make_args(B: int, K: int, *, target, draft=None, tokens, uniforms=None, temp
               target_strides: Sequence[int], draft_strides: Sequence[int] = (0, 0),
               length_mode: int = SV_LEN_FIXED, verify_len=None, confidence=None, tau=None,
               accepted_len, out_tokens, verify_len_out, lse_target=None, lse_draft=None, survival=None,
-              residual_mass=None, sampled_prob=None, device_status=None) -> Args:
+              residual_mass=None, sampled_prob=None, rows_read=None, device_status=None) -> Args:
     """Fill an Args struct.  Strides are (batch, row) in elements."""
     return Args(
         B, K, _addr(target), int(target_strides[0]), int(target_strides[1]),
@@ -117,7 +118,7 @@ def make_args(B: int, K: int, *, target, draft=None, tokens, uniforms=None, temp
         _addr(verify_len), _addr(confidence), _addr(tau),
         _addr(accepted_len), _addr(out_tokens), _addr(verify_len_out),
         _addr(lse_target), _addr(lse_draft), _addr(survival), _addr(residual_mass), _addr(sampled_prob),
-        _addr(device_status))
+        _addr(rows_read), _addr(device_status))
 
 
 def check(cfg: Config, args: Args) -> int:

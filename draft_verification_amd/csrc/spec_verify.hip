@@ -10,32 +10,40 @@
 // built around 16-byte coalesced loads, wavefront shuffles and small LDS
 // reductions.
 //
-// Pipeline of one call (four launches on the caller's stream):
-//   sv_plan     per-sequence set-up: verify length where it is known without
-//               reading logits, work-queue initialisation.
-//   sv_stream   persistent, queue-driven.  A queue entry is "position j of
-//               sequence b"; its items are fixed 16384-element splits of the
-//               target row and of the draft row.  Each item reduces its split
-//               to (max, sum exp) and the last item of an entry to finish merges
-//               the splits and takes the per-position decision: survival and
-//               verify length, the acceptance test u < p/q (or the greedy
-//               match), and what comes next.  Only then is position j+1 of that
-//               sequence put on the queue, so rows after the first rejection
-//               (and draft rows past the verify length) are never read.  The
-//               pages say generation restarts from the first error; nothing
-//               after it can change the output.
-//   sv_resid    per (rejecting sequence, split): sum of max(0, p - q) over the
-//               split of the rejected row pair.
-//   sv_draw     per sequence: inverse-CDF draw (replacement or bonus) by split
-//               prefix in fp64, then one 16384-element split re-read and scanned
-//               in token order; writes all outputs.
+// Early exit.  The pages say generation restarts from the first error, so no
+// row after the first rejection can change the output.  Positions are walked
+// in groups (sizes 2, 2, 4, 8, ... along the block); each group is two plain
+// launches:
+//   sv_rows    one workgroup per 16384-element split of every row the group
+//              needs (target and draft rows of sequences still open), reduced
+//              to (max, sum exp2) or (max, argmax) partials.  No atomics and no
+//              fences: the kernel boundary publishes the partials.
+//   sv_decide  one wavefront per open sequence: merges the partials of the
+//              group's positions in fp64 and walks them in order -- survival
+//              and verify length, the acceptance test u < p/q (or the greedy
+//              match) -- until the first rejection, the bonus row, or the end of
+//              the group.
+// Rows inside a group past a rejection are read speculatively (they lie within
+// the verify window).  Synchronising only at kernel boundaries keeps every
+// launch a pure stream: cross-XCD fences and hot atomics cost microseconds
+// each on this chip.
 //
-// Numerics.  bf16 and fp32 inputs are exact in fp32.  Per element the kernel
-// forms a = (l - m) * log2(e)/T with the constant split in two fp32 parts (so
-// the scale carries no systematic rounding bias) and takes v_exp_f32.  Sums run
-// in fp32 over 8 elements and in fp64 beyond, so a row sum carries ~1e-8
-// relative error.  Decisions (acceptance ratio, survival product, CDF prefix)
-// are taken in fp64.  The final draw evaluates large masses (> 2^-12) in fp64.
+// After the last group:
+//   sv_resid   per (rejecting sequence, split): sum of max(0, p - q) over the
+//              split of the rejected row pair.
+//   sv_draw    per sequence: inverse-CDF draw (replacement or bonus) by split
+//              prefix in fp64, then one split re-read and scanned in token
+//              order; writes the outputs.
+// sv_plan (first) sets up per-sequence state and the verify length where it
+// is known without reading logits.
+//
+// Numerics.  bf16 and fp32 inputs are exact in fp32.  Per element the kernels
+// form a = (l - m) * log2(e)/T with the constant split in two fp32 parts (so
+// the scale carries no systematic rounding bias) and take v_exp_f32 (measured
+// on MI355X: < 0.8 ulp for arguments >= -12).  Sums run in fp32 over 8
+// elements and in fp64 beyond, so a row sum carries ~1e-8 relative error.
+// Decisions (acceptance ratio, survival product, CDF prefix) are taken in fp64.
+// The final draw evaluates large masses (> 2^-12) in fp64.
 //
 // Determinism.  Split boundaries depend only on V, every reduction has a fixed
 // order and there are no floating-point atomics, so outputs are bitwise
@@ -52,19 +60,16 @@
 
 namespace {
 
-constexpr int kThreads = 256;              // 4 wavefronts of 64
+constexpr int kThreads = 256;                     // 4 wavefronts of 64
 constexpr int kWaves = kThreads / 64;
-constexpr int kSplit = 16384;              // elements per split (fixed for batch invariance)
-constexpr int kPerLane = kSplit / kThreads; // 64 elements per lane per split
-constexpr int kMaxSplits = SV_MAX_VOCAB / kSplit; // 64
-constexpr uint32_t kNeedT = 1u << 30;
-constexpr uint32_t kNeedD = 1u << 31;
-constexpr unsigned long long kTimeoutTicks = 400000000ull; // 4 s of the 100 MHz real-time counter
+constexpr int kSplit = 16384;                     // elements per split (fixed for batch invariance)
+constexpr int kPerLane = kSplit / kThreads;       // 64 elements per lane per split
+constexpr int kMaxGroup = 16;                     // positions per group
 
-enum { CTL_HEAD = 0, CTL_TAIL = 1, CTL_FINISHED = 2, CTL_STATUS = 3, CTL_WORDS = 64 };
+enum { CTL_STATUS = 0, CTL_WORDS = 64 };
 enum { FL_ACC = 1, FL_LEN = 2 };
 enum { KIND_NONE = -1, KIND_RESID = 0, KIND_BONUS = 1, KIND_GREEDY = 2, KIND_BAD = 3 };
-enum { K_PLAN = 0, K_STREAM = 1, K_RESID = 2, K_DRAW = 3, K_COUNT = 4 };
+enum { K_PLAN = 0, K_ROWS = 1, K_DECIDE = 2, K_RESID = 3, K_DRAW = 4, K_COUNT = 5 };
 
 struct SeqState {
     double S;      // survival product S_j of the positions evaluated so far
@@ -72,27 +77,25 @@ struct SeqState {
     float Mt, Md;  // maxima of those rows
     int L;         // verify length, -1 while undetermined
     int a;         // accepted positions so far
-    int flags;     // FL_ACC: acceptance walk open; FL_LEN: verify length open
+    int flags;     // FL_ACC: acceptance walk open; FL_LEN: verify-length walk open
     int kind;      // KIND_*
     int js;        // 1-based row of the final draw
-    int y;         // token chosen in sv_stream (greedy)
-    int e_final;   // queue entry that holds the final target row's split partials
+    int y;         // token chosen by the walk (greedy)
+    int rows;      // logit rows streamed for this sequence
     int pad;
 };
 
 struct Work {
     int* ctl;
-    uint32_t* queue;  // [entries] packed (b, j, need target, need draft), 0 = not yet published
-    int* cnt;         // [entries] finished items per entry
-    float* part_m;    // [entries][2][nsplit] split maxima (target, draft)
-    double* part_s;   // [entries][2][nsplit] split sums
-    int* part_i;      // [entries][nsplit] split argmax (greedy)
+    float* part_m;    // [B][2K+1][nsplit] split maxima; row j-1 target, K+j draft (j 1-based)
+    double* part_s;   // same layout, split sums of exp2((l - m) c)
+    int* part_i;      // same layout, split argmax (greedy)
     SeqState* st;     // [max_batch]
     double* rsum;     // [max_batch][nsplit] residual mass per split
 };
 
 struct Params {
-    int B, K, V, nsplit, ipe;  // ipe: items per queue entry
+    int B, K, V, nsplit;
     int greedy, derived;       // derived: tau mode with c = max draft probability
     int len_mode;
     const void* t;
@@ -114,23 +117,15 @@ struct Params {
     float* surv;
     float* zmass;
     float* pys;
+    int* rows_out;
     int* status_out;
 };
 
-// ---------------------------------------------------------------- memory model
+__device__ __forceinline__ void or_status(int* p, int v) { __hip_atomic_fetch_or(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
 
-__device__ __forceinline__ int ld_relaxed(const int* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
-__device__ __forceinline__ uint32_t ld_relaxed_u(const uint32_t* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
-__device__ __forceinline__ void st_relaxed_u(uint32_t* p, uint32_t v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
-__device__ __forceinline__ int add_relaxed(int* p, int v) { return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
-__device__ __forceinline__ int add_acq_rel(int* p, int v) { return __hip_atomic_fetch_add(p, v, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT); }
-__device__ __forceinline__ void or_relaxed(int* p, int v) { __hip_atomic_fetch_or(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
-__device__ __forceinline__ void fence_acquire() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
-__device__ __forceinline__ void fence_release() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
-
-__device__ __forceinline__ uint32_t enc_word(int b, int j, bool nt, bool nd)
+__device__ __forceinline__ long long part_index(const Params& p, int b, int row)
 {
-    return (uint32_t)b | ((uint32_t)j << 20) | (nt ? kNeedT : 0u) | (nd ? kNeedD : 0u);
+    return ((long long)b * (2 * p.K + 1) + row) * p.nsplit;
 }
 
 // ---------------------------------------------------------------- reductions
@@ -342,17 +337,7 @@ __device__ void split_argmax(const void* row, int V, int split, float& M, int& I
 __global__ __launch_bounds__(kThreads) void sv_plan_kernel(Params p, Work w)
 {
     const long long i = (long long)blockIdx.x * kThreads + threadIdx.x;
-    const long long ne = (long long)p.B * (p.K + 1);
-    if (i == 0) {
-        w.ctl[CTL_HEAD] = 0;
-        w.ctl[CTL_TAIL] = p.B;
-        w.ctl[CTL_FINISHED] = 0;
-        w.ctl[CTL_STATUS] = 0;
-    }
-    if (i < ne) {
-        w.cnt[i] = 0;
-        if (i >= p.B) w.queue[i] = 0u;
-    }
+    if (i == 0) w.ctl[CTL_STATUS] = 0;
     if (i >= p.B) return;
     const int b = (int)i, K = p.K;
     SeqState st;
@@ -363,7 +348,7 @@ __global__ __launch_bounds__(kThreads) void sv_plan_kernel(Params p, Work w)
     st.kind = KIND_NONE;
     st.js = 0;
     st.y = -1;
-    st.e_final = -1;
+    st.rows = 0;
     st.pad = 0;
     bool bad = false, len_open = false;
     int L;
@@ -392,112 +377,174 @@ __global__ __launch_bounds__(kThreads) void sv_plan_kernel(Params p, Work w)
     if (bad) {
         st.kind = KIND_BAD;
         st.flags = 0;
-        or_relaxed(&w.ctl[CTL_STATUS], SV_STATUS_BAD_INPUT);
+        or_status(&w.ctl[CTL_STATUS], SV_STATUS_BAD_INPUT);
     } else {
         st.flags = FL_ACC | (len_open ? FL_LEN : 0);
     }
     w.st[b] = st;
-    const bool nt = !bad;
-    const bool nd = !bad && !p.greedy && (len_open || L >= 1);
-    w.queue[b] = enc_word(b, 1, nt, nd);
 }
 
-// ---------------------------------------------------------------- sv_stream
+// ---------------------------------------------------------------- sv_rows
 //
-// Per-position decision, run by the workgroup that finishes the last item of
-// queue entry e = (b, j).  Wave 0 merges the split partials; thread 0 updates
-// the sequence state and publishes (b, j+1) or retires the sequence.
+// Which rows of a group are streamed, from the state at the start of the group:
+//   target row j  iff the acceptance walk is open and (L unknown or j <= L+1)
+//   draft row j   iff j <= K and (the length walk is open, or the acceptance
+//                 walk is open and j <= L)
+// sv_decide uses the same state, so every row its walk touches was streamed.
 
-template <int DT, bool GREEDY>
-__device__ void decide(const Params& p, const Work& w, int e, int b, int j, bool nt, bool nd)
+__device__ __forceinline__ bool target_row_needed(int flags, int L, int j, int K)
 {
-    __shared__ float s_Mt, s_Md;
-    __shared__ double s_St, s_Sd;
-    __shared__ int s_g;
-    const int lane = threadIdx.x;
-    if (lane < 64) {
-        const bool has = lane < p.nsplit;
-        if (nt) {
-            const long long pb = ((long long)e * 2 + 0) * p.nsplit + lane;
-            if (GREEDY) {
-                float v = has ? w.part_m[pb] : -INFINITY;
-                int ix = has ? w.part_i[(long long)e * p.nsplit + lane] : 0x7fffffff;
-                wave_argmax(v, ix);
-                if (lane == 0) { s_Mt = v; s_g = ix; }
-            } else {
-                const float m = has ? w.part_m[pb] : -INFINITY;
-                const float M = wave_max(m);
-                double s = 0.0;
-                if (has && m != -INFINITY) s = w.part_s[pb] * exp2(((double)m - (double)M) * p.c64);
-                s = wave_sum(s);
-                if (lane == 0) { s_Mt = M; s_St = s; }
-            }
+    return (flags & FL_ACC) && j <= K + 1 && (L < 0 || j <= L + 1);
+}
+
+__device__ __forceinline__ bool draft_row_needed(int flags, int L, int j, int K)
+{
+    return j <= K && ((flags & FL_LEN) || ((flags & FL_ACC) && j <= L));
+}
+
+template <int DT, bool VEC, bool GREEDY>
+__global__ __launch_bounds__(kThreads) void sv_rows_kernel(Params p, Work w, int j0, int G)
+{
+    __shared__ float redf[kWaves];
+    __shared__ double redd[kWaves];
+    __shared__ int redi[kWaves];
+    const int split = (int)(blockIdx.x % p.nsplit);
+    const int rest = (int)(blockIdx.x / p.nsplit);
+    const int slots = GREEDY ? G : 2 * G;
+    const int slot = rest % slots;
+    const int b = rest / slots;
+    const bool draft = !GREEDY && slot >= G;
+    const int j = j0 + (draft ? slot - G : slot); // 1-based position
+    const int flags = w.st[b].flags;
+    const int L = w.st[b].L;
+    const bool need = draft ? draft_row_needed(flags, L, j, p.K) : target_row_needed(flags, L, j, p.K);
+    if (!need) return;
+    const void* row = draft ? row_ptr<DT>(p.d, p.dbs, p.drs, b, j - 1) : row_ptr<DT>(p.t, p.tbs, p.trs, b, j - 1);
+    const long long pi = part_index(p, b, draft ? p.K + j : j - 1) + split;
+    if (GREEDY) {
+        float M;
+        int I;
+        split_argmax<DT, VEC>(row, p.V, split, M, I, redf, redi);
+        if (threadIdx.x == 0) {
+            w.part_m[pi] = M;
+            w.part_i[pi] = I;
         }
-        if (!GREEDY && nd) {
-            const long long pb = ((long long)e * 2 + 1) * p.nsplit + lane;
-            const float m = has ? w.part_m[pb] : -INFINITY;
-            const float M = wave_max(m);
-            double s = 0.0;
-            if (has && m != -INFINITY) s = w.part_s[pb] * exp2(((double)m - (double)M) * p.c64);
-            s = wave_sum(s);
-            if (lane == 0) { s_Md = M; s_Sd = s; }
+    } else {
+        float M;
+        double S;
+        split_stats<DT, VEC>(row, p.V, split, p.c_hi, p.c_lo, M, S, redf, redd);
+        if (threadIdx.x == 0) {
+            w.part_m[pi] = M;
+            w.part_s[pi] = S;
         }
     }
-    __syncthreads();
-    if (threadIdx.x != 0) return;
+}
 
+// ---------------------------------------------------------------- sv_decide
+//
+// One wavefront per sequence.  Lanes merge the split partials of the group's
+// positions in parallel (fixed order, fp64) and gather the drafted tokens'
+// logits; lane 0 then walks the positions in order.
+
+template <int DT, bool GREEDY>
+__global__ __launch_bounds__(64) void sv_decide_kernel(Params p, Work w, int j0, int G)
+{
+    __shared__ float sMt[kMaxGroup], sMd[kMaxGroup], sLt[kMaxGroup], sLd[kMaxGroup];
+    __shared__ double sSt[kMaxGroup], sSd[kMaxGroup];
+    __shared__ int sG[kMaxGroup];
+    const int b = blockIdx.x, lane = threadIdx.x, K = p.K;
     SeqState st = w.st[b];
     bool acc = (st.flags & FL_ACC) != 0;
     bool len = (st.flags & FL_LEN) != 0;
-    const int K = p.K;
-    const float Mt = s_Mt, Md = s_Md;
-    const double St = s_St, Sd = s_Sd;
+    if (!acc && !len) return;
+    const int n = min(j0 + G - 1, K + 1) - j0 + 1;
+    const int flags0 = st.flags, L0 = st.L;
 
-    if (!GREEDY) {
-        if (nt && p.lse_t) p.lse_t[(long long)b * (K + 1) + (j - 1)] = (float)((double)Mt * p.invT64 + log(St));
-        if (nd && p.lse_d) p.lse_d[(long long)b * K + (j - 1)] = (float)((double)Md * p.invT64 + log(Sd));
-        if (nd && p.derived) {
-            // c_j = max_v q_j(v) = 1 / Sd; S_j = S_{j-1} c_j
-            const double S = st.S / Sd;
-            st.S = S;
-            if (p.surv) p.surv[(long long)b * K + (j - 1)] = (float)S;
-            if (len) {
-                if (S >= (double)p.tau[b]) {
-                    if (j == K) { st.L = K; len = false; }
-                } else {
-                    st.L = j - 1;
-                    len = false;
+    for (int pair = lane; pair < 2 * n; pair += 64) {
+        const int q = pair >> 1, kind = pair & 1, j = j0 + q;
+        const bool read = kind ? (!GREEDY && draft_row_needed(flags0, L0, j, K)) : target_row_needed(flags0, L0, j, K);
+        if (!read) continue;
+        const long long base = part_index(p, b, kind ? K + j : j - 1);
+        if (GREEDY) {
+            float bv = -INFINITY;
+            int bi = 0x7fffffff;
+            for (int k = 0; k < p.nsplit; ++k) {
+                const float v = w.part_m[base + k];
+                const int ix = w.part_i[base + k];
+                if (v > bv || (v == bv && ix < bi)) { bv = v; bi = ix; }
+            }
+            sMt[q] = bv;
+            sG[q] = bi;
+        } else {
+            float M = -INFINITY;
+            for (int k = 0; k < p.nsplit; ++k) M = fmaxf(M, w.part_m[base + k]);
+            double S = 0.0;
+            for (int k = 0; k < p.nsplit; ++k) {
+                const float m = w.part_m[base + k];
+                if (m != -INFINITY) S += w.part_s[base + k] * exp2(((double)m - (double)M) * p.c64);
+            }
+            if (kind) { sMd[q] = M; sSd[q] = S; }
+            else { sMt[q] = M; sSt[q] = S; }
+            if (j <= K) {
+                const int x = p.tok[(long long)b * K + (j - 1)];
+                if (x >= 0 && x < p.V) {
+                    if (kind) sLd[q] = load_one<DT>(row_ptr<DT>(p.d, p.dbs, p.drs, b, j - 1), x);
+                    else sLt[q] = load_one<DT>(row_ptr<DT>(p.t, p.tbs, p.trs, b, j - 1), x);
                 }
             }
         }
     }
+    __syncthreads();
+    if (lane != 0) return;
 
-    if (acc && nt) {
-        const bool verify = len || st.L >= j; // open walk means S_j >= tau, so L >= j
+    for (int q = 0; q < n; ++q) {
+        const int j = j0 + q;
+        const bool dread = !GREEDY && draft_row_needed(flags0, L0, j, K);
+        st.rows += (target_row_needed(flags0, L0, j, K) ? 1 : 0) + (dread ? 1 : 0);
+        if (!acc && !len) continue; // rows of this group past the stop were still streamed
+        if (!GREEDY) {
+            if (acc && p.lse_t) p.lse_t[(long long)b * (K + 1) + (j - 1)] = (float)((double)sMt[q] * p.invT64 + log(sSt[q]));
+            if (dread && p.lse_d) p.lse_d[(long long)b * K + (j - 1)] = (float)((double)sMd[q] * p.invT64 + log(sSd[q]));
+            if (dread && p.derived) {
+                // c_j = max_v q_j(v) = 1 / Sd; S_j = S_{j-1} c_j
+                const double S = st.S / sSd[q];
+                st.S = S;
+                if (p.surv) p.surv[(long long)b * K + (j - 1)] = (float)S;
+                if (len) {
+                    if (S >= (double)p.tau[b]) {
+                        if (j == K) { st.L = K; len = false; }
+                    } else {
+                        st.L = j - 1;
+                        len = false;
+                    }
+                }
+            }
+        }
+        if (!acc) continue;
+        const bool verify = len || st.L >= j; // open length walk means S_j >= tau, so L >= j
         if (verify) {
             const int x = p.tok[(long long)b * K + (j - 1)];
             if (x < 0 || x >= p.V) {
                 st.kind = KIND_BAD;
                 st.a = 0;
                 acc = false;
-                or_relaxed(&w.ctl[CTL_STATUS], SV_STATUS_BAD_INPUT);
+                or_status(&w.ctl[CTL_STATUS], SV_STATUS_BAD_INPUT);
             } else if (GREEDY) {
-                if (x == s_g) {
+                if (x == sG[q]) {
                     st.a = j;
                 } else {
                     st.kind = KIND_GREEDY;
-                    st.y = s_g;
+                    st.y = sG[q];
                     acc = false;
                 }
             } else {
-                const float lt = load_one<DT>(row_ptr<DT>(p.t, p.tbs, p.trs, b, j - 1), x);
-                const float ld = load_one<DT>(row_ptr<DT>(p.d, p.dbs, p.drs, b, j - 1), x);
+                const float lt = sLt[q], ld = sLd[q];
                 double ratio;
                 if (ld == -INFINITY) {
                     ratio = INFINITY; // q(x) = 0
                 } else {
-                    const double dlt = (double)lt - (double)Mt, dld = (double)ld - (double)Md;
-                    ratio = exp2((dlt - dld) * p.c64) * (Sd / St);
+                    const double dlt = (double)lt - (double)sMt[q], dld = (double)ld - (double)sMd[q];
+                    ratio = exp2((dlt - dld) * p.c64) * (sSd[q] / sSt[q]);
                 }
                 const double uj = (double)p.u[(long long)b * (K + 1) + (j - 1)];
                 if (uj < ratio) {
@@ -505,8 +552,7 @@ __device__ void decide(const Params& p, const Work& w, int e, int b, int j, bool
                 } else {
                     st.kind = KIND_RESID;
                     st.js = j;
-                    st.Mt = Mt; st.St = St; st.Md = Md; st.Sd = Sd;
-                    st.e_final = e;
+                    st.Mt = sMt[q]; st.St = sSt[q]; st.Md = sMd[q]; st.Sd = sSd[q];
                     acc = false;
                 }
             }
@@ -514,114 +560,17 @@ __device__ void decide(const Params& p, const Work& w, int e, int b, int j, bool
             // L == j - 1: the final token comes from target row j
             if (GREEDY) {
                 st.kind = KIND_GREEDY;
-                st.y = s_g;
+                st.y = sG[q];
             } else {
                 st.kind = KIND_BONUS;
                 st.js = j;
-                st.Mt = Mt; st.St = St;
-                st.e_final = e;
+                st.Mt = sMt[q]; st.St = sSt[q];
             }
             acc = false;
         }
     }
-
     st.flags = (acc ? FL_ACC : 0) | (len ? FL_LEN : 0);
     w.st[b] = st;
-    if (acc || len) {
-        const int jn = j + 1;
-        const bool ntn = acc;
-        const bool ndn = !GREEDY && jn <= K && (len || (acc && st.L >= jn));
-        const int slot = add_relaxed(&w.ctl[CTL_TAIL], 1);
-        fence_release(); // the state above before the queue word
-        st_relaxed_u(&w.queue[slot], enc_word(b, jn, ntn, ndn));
-    } else {
-        fence_release();
-        add_relaxed(&w.ctl[CTL_FINISHED], 1);
-    }
-}
-
-template <int DT, bool VEC, bool GREEDY>
-__global__ __launch_bounds__(kThreads) void sv_stream_kernel(Params p, Work w)
-{
-    __shared__ float redf[kWaves];
-    __shared__ double redd[kWaves];
-    __shared__ int redi[kWaves];
-    __shared__ int s_cmd, s_sub, s_e, s_last;
-    __shared__ uint32_t s_word;
-    const long long entries = (long long)p.B * (p.K + 1);
-
-    for (;;) {
-        if (threadIdx.x == 0) {
-            const int item = add_relaxed(&w.ctl[CTL_HEAD], 1);
-            const long long e = item / p.ipe;
-            int cmd = 0;
-            uint32_t word = 0;
-            if (e >= entries) {
-                cmd = 1;
-            } else {
-                const unsigned long long t0 = wall_clock64();
-                for (;;) {
-                    word = ld_relaxed_u(&w.queue[e]);
-                    if (word) break;
-                    if (ld_relaxed(&w.ctl[CTL_FINISHED]) >= p.B) { cmd = 1; break; }
-                    if (wall_clock64() - t0 > kTimeoutTicks) {
-                        or_relaxed(&w.ctl[CTL_STATUS], SV_STATUS_TIMEOUT);
-                        cmd = 1;
-                        break;
-                    }
-                    __builtin_amdgcn_s_sleep(4);
-                }
-                if (!cmd) fence_acquire();
-            }
-            s_cmd = cmd;
-            s_word = word;
-            s_sub = item % p.ipe;
-            s_e = (int)e;
-        }
-        __syncthreads();
-        if (s_cmd) return;
-        const uint32_t word = s_word;
-        const int sub = s_sub, e = s_e;
-        __syncthreads();
-
-        const int b = (int)(word & 0xFFFFFu);
-        const int j = (int)((word >> 20) & 0x3FFu);
-        const bool nt = (word & kNeedT) != 0, nd = (word & kNeedD) != 0;
-        const int kind = GREEDY ? 0 : sub / p.nsplit;
-        const int split = GREEDY ? sub : sub % p.nsplit;
-        if (kind == 0 ? nt : nd) {
-            if (GREEDY) {
-                float M;
-                int I;
-                split_argmax<DT, VEC>(row_ptr<DT>(p.t, p.tbs, p.trs, b, j - 1), p.V, split, M, I, redf, redi);
-                if (threadIdx.x == 0) {
-                    w.part_m[((long long)e * 2) * p.nsplit + split] = M;
-                    w.part_i[(long long)e * p.nsplit + split] = I;
-                }
-            } else {
-                const void* row = kind == 0 ? row_ptr<DT>(p.t, p.tbs, p.trs, b, j - 1)
-                                            : row_ptr<DT>(p.d, p.dbs, p.drs, b, j - 1);
-                float M;
-                double S;
-                split_stats<DT, VEC>(row, p.V, split, p.c_hi, p.c_lo, M, S, redf, redd);
-                if (threadIdx.x == 0) {
-                    const long long pi = ((long long)e * 2 + kind) * p.nsplit + split;
-                    w.part_m[pi] = M;
-                    w.part_s[pi] = S;
-                }
-            }
-        }
-        if (threadIdx.x == 0) {
-            const int old = add_acq_rel(&w.cnt[e], 1); // releases this item's partial
-            s_last = (old == p.ipe - 1);
-        }
-        __syncthreads();
-        if (s_last) {
-            fence_acquire();
-            decide<DT, GREEDY>(p, w, e, b, j, nt, nd);
-        }
-        __syncthreads();
-    }
 }
 
 // ---------------------------------------------------------------- final draw
@@ -629,27 +578,9 @@ __global__ __launch_bounds__(kThreads) void sv_stream_kernel(Params p, Work w)
 struct DrawCtx {
     float Mt, Md, invSt, invSd, c_hi, c_lo;
     double St, Sd, c64;
-    bool resid;
 };
 
-__device__ __noinline__ double draw_mass_f64(float lt, float ld, const DrawCtx& c)
-{
-    const double pd = exp2(((double)lt - (double)c.Mt) * c.c64) / c.St;
-    const double qd = c.resid ? exp2(((double)ld - (double)c.Md) * c.c64) / c.Sd : 0.0;
-    return pd > qd ? pd - qd : 0.0;
-}
-
-// Mass of one token under the final draw: max(0, p - q) for a replacement,
-// p for a bonus.  fp32 first; masses above 2^-12 are recomputed in fp64.
-__device__ __forceinline__ double draw_mass(float lt, float ld, const DrawCtx& c)
-{
-    const float pf = scaled_exp2(lt, c.Mt, c.c_hi, c.c_lo) * c.invSt;
-    const float qf = c.resid ? scaled_exp2(ld, c.Md, c.c_hi, c.c_lo) * c.invSd : 0.0f;
-    if (fmaxf(pf, qf) > 0x1p-12f) return draw_mass_f64(lt, ld, c);
-    return pf > qf ? (double)(pf - qf) : 0.0;
-}
-
-__device__ __forceinline__ DrawCtx make_ctx(const SeqState& st, const Params& p, bool resid)
+__device__ __forceinline__ DrawCtx make_ctx(const SeqState& st, const Params& p)
 {
     DrawCtx c;
     c.Mt = st.Mt;
@@ -657,12 +588,29 @@ __device__ __forceinline__ DrawCtx make_ctx(const SeqState& st, const Params& p,
     c.St = st.St;
     c.Sd = st.Sd;
     c.invSt = (float)(1.0 / st.St);
-    c.invSd = resid ? (float)(1.0 / st.Sd) : 0.0f;
+    c.invSd = st.Sd > 0.0 ? (float)(1.0 / st.Sd) : 0.0f;
     c.c_hi = p.c_hi;
     c.c_lo = p.c_lo;
     c.c64 = p.c64;
-    c.resid = resid;
     return c;
+}
+
+__device__ __forceinline__ double mass_f64(float lt, float ld, const DrawCtx& c, bool resid)
+{
+    const double pd = exp2(((double)lt - (double)c.Mt) * c.c64) / c.St;
+    const double qd = resid ? exp2(((double)ld - (double)c.Md) * c.c64) / c.Sd : 0.0;
+    return pd > qd ? pd - qd : 0.0;
+}
+
+// Mass of one token under the final draw: max(0, p - q) for a replacement,
+// p for a bonus.  fp32 first; masses whose p or q exceeds 2^-12 are evaluated
+// in fp64 (at most 2^13 tokens of a row pair qualify).
+__device__ __forceinline__ double draw_mass(float lt, float ld, const DrawCtx& c, bool resid)
+{
+    const float pf = scaled_exp2(lt, c.Mt, c.c_hi, c.c_lo) * c.invSt;
+    const float qf = resid ? scaled_exp2(ld, c.Md, c.c_hi, c.c_lo) * c.invSd : 0.0f;
+    if (fmaxf(pf, qf) > 0x1p-12f) return mass_f64(lt, ld, c, resid);
+    return pf > qf ? (double)(pf - qf) : 0.0;
 }
 
 template <int DT, bool VEC>
@@ -671,27 +619,75 @@ __global__ __launch_bounds__(kThreads) void sv_resid_kernel(Params p, Work w)
     __shared__ double redd[kWaves];
     const int b = (int)(blockIdx.x / p.nsplit);
     const int split = (int)(blockIdx.x % p.nsplit);
+    if (w.st[b].kind != KIND_RESID) return;
     const SeqState st = w.st[b];
-    if (st.kind != KIND_RESID) return;
-    const DrawCtx c = make_ctx(st, p, true);
+    const DrawCtx c = make_ctx(st, p);
     Chunk<DT> tc, dc;
     tc.template load<VEC>(row_ptr<DT>(p.t, p.tbs, p.trs, b, st.js - 1), split * kSplit, p.V, threadIdx.x);
     dc.template load<VEC>(row_ptr<DT>(p.d, p.dbs, p.drs, b, st.js - 1), split * kSplit, p.V, threadIdx.x);
     double acc = 0.0;
 #pragma unroll
-    for (int e = 0; e < kPerLane; ++e) acc += draw_mass(tc.get(e), dc.get(e), c);
+    for (int e = 0; e < kPerLane; ++e) acc += draw_mass(tc.get(e), dc.get(e), c, true);
     acc = block_sum(acc, redd);
     if (threadIdx.x == 0) w.rsum[(long long)b * p.nsplit + split] = acc;
 }
 
-template <int DT>
+// Inclusive prefix sum over the 64 lanes of a wavefront (fixed order).
+__device__ __forceinline__ double wave_incl_scan(double v, int lane)
+{
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const double n = __shfl_up(v, o);
+        if (lane >= o) v += n;
+    }
+    return v;
+}
+
+// 64 consecutive elements of a row starting at i0 (thread-contiguous layout).
+template <int DT, bool VEC>
+struct Run {
+    float v[64];
+    __device__ __forceinline__ void load(const void* row, int i0, int V)
+    {
+        if (DT == SV_BF16) {
+            const uint16_t* r = (const uint16_t*)row;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int i = i0 + 8 * k;
+                if (VEC && i < V) {
+                    const uint4 q = *(const uint4*)(r + i);
+                    const uint32_t ws[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+                    for (int h = 0; h < 4; ++h) { v[8 * k + 2 * h] = bf16_lo(ws[h]); v[8 * k + 2 * h + 1] = bf16_hi(ws[h]); }
+                } else {
+#pragma unroll
+                    for (int h = 0; h < 8; ++h) v[8 * k + h] = (i + h < V) ? bf16_lo((uint32_t)r[i + h]) : -INFINITY;
+                }
+            }
+        } else {
+            const float* r = (const float*)row;
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                const int i = i0 + 4 * k;
+                if (VEC && i < V) {
+                    const float4 q = *(const float4*)(r + i);
+                    v[4 * k] = q.x; v[4 * k + 1] = q.y; v[4 * k + 2] = q.z; v[4 * k + 3] = q.w;
+                } else {
+#pragma unroll
+                    for (int h = 0; h < 4; ++h) v[4 * k + h] = (i + h < V) ? r[i + h] : -INFINITY;
+                }
+            }
+        }
+    }
+};
+
+template <int DT, bool VEC>
 __global__ __launch_bounds__(kThreads) void sv_draw_kernel(Params p, Work w)
 {
-    __shared__ double s_mass[kMaxSplits];
-    __shared__ double s_tsum[kThreads];
-    __shared__ double s_wrel, s_prefix, s_Z, s_my;
-    __shared__ int s_split, s_tstar, s_resid, s_y;
-    const int b = blockIdx.x;
+    __shared__ double s_wtot[kWaves];
+    __shared__ double s_wrel, s_Z, s_my;
+    __shared__ int s_split, s_resid, s_first[kWaves], s_lastpos[kWaves], s_y;
+    const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int K = p.K;
     const SeqState st = w.st[b];
     int kind = st.kind;
@@ -700,96 +696,102 @@ __global__ __launch_bounds__(kThreads) void sv_draw_kernel(Params p, Work w)
     float zrep = NAN, py = NAN;
 
     if (kind == KIND_RESID || kind == KIND_BONUS) {
-        if (threadIdx.x == 0) {
+        // 1. masses of the splits and the split that holds the draw point (wave 0)
+        if (wv == 0) {
             bool resid = kind == KIND_RESID;
-            double Z = 0.0;
-            if (resid) {
-                for (int k = 0; k < p.nsplit; ++k) {
-                    s_mass[k] = w.rsum[(long long)b * p.nsplit + k];
-                    Z += s_mass[k];
-                }
-                if (!(Z > 0.0)) resid = false; // cannot happen in exact arithmetic after a rejection
-            }
+            double m = (resid && lane < p.nsplit) ? w.rsum[(long long)b * p.nsplit + lane] : 0.0;
+            double incl = wave_incl_scan(m, lane);
+            const double Z = __shfl(incl, p.nsplit - 1);
+            if (resid && !(Z > 0.0)) resid = false; // cannot happen in exact arithmetic after a rejection
             if (!resid) {
-                // masses of p per split from the stream pass: s_k 2^((m_k - M) c) / S
-                const long long pb = ((long long)st.e_final * 2) * p.nsplit;
-                for (int k = 0; k < p.nsplit; ++k) {
-                    const float m = w.part_m[pb + k];
-                    s_mass[k] = m == -INFINITY ? 0.0 : w.part_s[pb + k] * exp2(((double)m - (double)st.Mt) * p.c64) / st.St;
+                m = 0.0;
+                if (lane < p.nsplit) {
+                    const long long pb = part_index(p, b, st.js - 1) + lane;
+                    const float mk = w.part_m[pb];
+                    if (mk != -INFINITY) m = w.part_s[pb] * exp2(((double)mk - (double)st.Mt) * p.c64) / st.St;
                 }
+                incl = wave_incl_scan(m, lane);
             }
             const double uf = (double)p.u[(long long)b * (K + 1) + K];
             const double target = resid ? uf * Z : uf;
-            double C = 0.0, wrel = INFINITY;
-            int ks = -1;
-            for (int k = 0; k < p.nsplit; ++k) {
-                const double Cn = C + s_mass[k];
-                if (Cn > target) { ks = k; wrel = target - C; break; }
-                C = Cn;
-            }
-            if (ks < 0) { // rounding: take the last token with mass
-                for (int k = p.nsplit - 1; k >= 0; --k)
-                    if (s_mass[k] > 0.0) { ks = k; break; }
-                if (ks < 0) ks = 0;
+            const double up = __shfl_up(incl, 1); // every lane takes part in the shuffle
+            const double excl = lane == 0 ? 0.0 : up;
+            const unsigned long long pass = __ballot(lane < p.nsplit && incl > target);
+            int ks;
+            double wrel;
+            if (pass) {
+                ks = __ffsll(pass) - 1;
+                wrel = target - __shfl(excl, ks);
+            } else { // rounding: the last split with mass, its last token
+                const unsigned long long pos = __ballot(lane < p.nsplit && m > 0.0);
+                ks = pos ? 63 - __clzll(pos) : 0;
                 wrel = INFINITY;
             }
-            s_split = ks;
-            s_wrel = wrel;
-            s_resid = resid ? 1 : 0;
-            s_Z = kind == KIND_RESID ? (resid ? Z : 0.0) : 1.0;
+            if (lane == 0) {
+                s_split = ks;
+                s_wrel = wrel;
+                s_resid = resid ? 1 : 0;
+                s_Z = kind == KIND_RESID ? (resid ? Z : 0.0) : 1.0;
+            }
         }
         __syncthreads();
         const bool resid = s_resid != 0;
-        const DrawCtx c = make_ctx(st, p, resid);
+        const DrawCtx c = make_ctx(st, p);
         const void* trow = row_ptr<DT>(p.t, p.tbs, p.trs, b, st.js - 1);
         const void* drow = resid ? row_ptr<DT>(p.d, p.dbs, p.drs, b, st.js - 1) : nullptr;
-        const int base = s_split * kSplit + threadIdx.x * kPerLane;
-        const int end = min(base + kPerLane, p.V);
+        const int i0 = s_split * kSplit + tid * 64;
+        const double wrel = s_wrel;
+
+        // 2. thread sums over 64 consecutive tokens, then a fixed-order block scan
+        Run<DT, VEC> tr, dr;
+        tr.load(trow, i0, p.V);
+        if (resid) dr.load(drow, i0, p.V);
         double s = 0.0;
         int last_pos = -1;
-        for (int i = base; i < end; ++i) {
-            const double m = draw_mass(load_one<DT>(trow, i), resid ? load_one<DT>(drow, i) : 0.0f, c);
-            s += m;
-            if (m > 0.0) last_pos = i;
+#pragma unroll
+        for (int e = 0; e < 64; ++e) {
+            const double mv = draw_mass(tr.v[e], resid ? dr.v[e] : 0.0f, c, resid);
+            s += mv;
+            if (mv > 0.0) last_pos = i0 + e;
         }
-        s_tsum[threadIdx.x] = s;
+        const double incl = wave_incl_scan(s, lane);
+        if (lane == 63) s_wtot[wv] = incl;
         __syncthreads();
-        if (threadIdx.x == 0) {
-            double P = 0.0, wrel = s_wrel;
-            int ts = -1;
-            for (int t = 0; t < kThreads; ++t) {
-                if (P + s_tsum[t] > wrel) { ts = t; break; }
-                P += s_tsum[t];
-            }
-            if (ts < 0) {
-                wrel = INFINITY;
-                P = 0.0;
-                for (int t = kThreads - 1; t >= 0; --t)
-                    if (s_tsum[t] > 0.0) { ts = t; break; }
-                if (ts < 0) ts = 0;
-                for (int t = 0; t < ts; ++t) P += s_tsum[t];
-            }
-            s_tstar = ts;
-            s_prefix = P;
-            s_wrel = wrel;
+        double woff = 0.0;
+        for (int k = 0; k < wv; ++k) woff += s_wtot[k];
+        const double up = __shfl_up(incl, 1); // every lane takes part in the shuffle
+        const double prefix = woff + (lane == 0 ? 0.0 : up);
+        const unsigned long long pass = __ballot(prefix + s > wrel);
+        const unsigned long long pos = __ballot(s > 0.0);
+        if (lane == 0) {
+            s_first[wv] = pass ? wv * 64 + __ffsll(pass) - 1 : 0x7fffffff;
+            s_lastpos[wv] = pos ? wv * 64 + 63 - __clzll(pos) : -1;
         }
         __syncthreads();
-        if ((int)threadIdx.x == s_tstar) {
-            const double P = s_prefix, wrel = s_wrel;
-            double cl = 0.0, my;
+        int tstar = 0x7fffffff, tlast = -1;
+        for (int k = 0; k < kWaves; ++k) {
+            tstar = min(tstar, s_first[k]);
+            tlast = max(tlast, s_lastpos[k]);
+        }
+        const bool fallback = wrel == INFINITY || tstar == 0x7fffffff;
+        if (fallback) tstar = tlast >= 0 ? tlast : 0;
+
+        // 3. the thread that holds the crossing walks its tokens in order
+        if (tid == tstar) {
             int yy = -1;
-            if (wrel != INFINITY) {
-                for (int i = base; i < end; ++i) {
-                    const double m = draw_mass(load_one<DT>(trow, i), resid ? load_one<DT>(drow, i) : 0.0f, c);
-                    cl += m;
-                    if (P + cl > wrel) { yy = i; break; }
+            if (!fallback) {
+                double cl = 0.0;
+#pragma unroll
+                for (int e = 0; e < 64; ++e) {
+                    const double mv = draw_mass(tr.v[e], resid ? dr.v[e] : 0.0f, c, resid);
+                    cl += mv;
+                    if (yy < 0 && prefix + cl > wrel) yy = i0 + e;
                 }
             }
-            if (yy < 0) yy = last_pos >= 0 ? last_pos : base;
-            // the reported probability of the chosen token is always evaluated in fp64
-            my = draw_mass_f64(load_one<DT>(trow, yy), resid ? load_one<DT>(drow, yy) : 0.0f, c);
+            if (yy < 0) yy = last_pos >= 0 ? last_pos : i0;
             s_y = yy;
-            s_my = my;
+            // the reported probability of the chosen token is evaluated in fp64
+            s_my = mass_f64(load_one<DT>(trow, yy), resid ? load_one<DT>(drow, yy) : 0.0f, c, resid);
         }
         __syncthreads();
         y = s_y;
@@ -803,38 +805,36 @@ __global__ __launch_bounds__(kThreads) void sv_draw_kernel(Params p, Work w)
         y = -1;
     }
 
-    for (int jj = threadIdx.x; jj <= K; jj += kThreads) {
+    for (int jj = tid; jj <= K; jj += kThreads) {
         int v = -1;
         if (y >= 0) v = jj < a ? p.tok[(long long)b * K + jj] : (jj == a ? y : -1);
         p.out_tok[(long long)b * (K + 1) + jj] = v;
     }
-    if (threadIdx.x == 0) {
+    if (tid == 0) {
         p.acc_out[b] = a;
         p.vl_out[b] = st.L;
         if (p.zmass) p.zmass[b] = zrep;
         if (p.pys) p.pys[b] = py;
+        if (p.rows_out) p.rows_out[b] = st.rows;
         if (b == 0 && p.status_out) *p.status_out = w.ctl[CTL_STATUS];
     }
 }
 
 // ---------------------------------------------------------------- host side
 
-const char* const kKernelNames[K_COUNT] = {"sv_plan", "sv_stream", "sv_resid", "sv_draw"};
-
-template <int DT, bool VEC, bool G>
-const void* stream_fn() { return (const void*)sv_stream_kernel<DT, VEC, G>; }
+const char* const kKernelNames[K_COUNT] = {"sv_plan", "sv_rows", "sv_decide", "sv_resid", "sv_draw"};
+constexpr int kMaxSlots = 64; // timed launches per run
 
 } // namespace
 
 struct spec_verify {
     spec_verify_config cfg;
     int nsplit;
-    int cus;
-    int occ[2][2];        // [vec][greedy] resident workgroups per CU of sv_stream
     void* ws;
     Work w;
     int timing_max, timing_n;
-    hipEvent_t* ev;       // [timing_max][K_COUNT][2]
+    hipEvent_t* ev;       // [timing_max][kMaxSlots][2]
+    int* ev_kernel;       // [timing_max][kMaxSlots] kernel id of each timed launch, -1 unused
 };
 
 namespace {
@@ -899,8 +899,10 @@ static int check_config(const spec_verify_config* cfg)
     if (cfg->vocab < 1 || cfg->vocab > SV_MAX_VOCAB) return SV_EINVAL;
     if (cfg->dtype != SV_F32 && cfg->dtype != SV_BF16) return SV_EUNSUPPORTED;
     if (cfg->device < 0) return SV_EINVAL;
-    const long long items = (long long)cfg->max_batch * (cfg->max_draft + 1) * 2 * nsplit_of(cfg->vocab);
-    if (items > (1ll << 30)) return SV_EUNSUPPORTED;
+    const long long grid = (long long)cfg->max_batch * 2 * kMaxGroup * nsplit_of(cfg->vocab);
+    if (grid > 0x7fffffffll) return SV_EUNSUPPORTED; // largest sv_rows grid
+    const long long nres = (long long)cfg->max_batch * nsplit_of(cfg->vocab);
+    if (nres > 0x7fffffffll) return SV_EUNSUPPORTED;
     return SV_OK;
 }
 
@@ -943,39 +945,18 @@ int spec_verify_create(const spec_verify_config* cfg, spec_verify_t** out)
     if (!h) return SV_ENOMEM;
     h->cfg = *cfg;
     h->nsplit = nsplit_of(cfg->vocab);
-    hipDeviceProp_t prop;
-    if (hipGetDeviceProperties(&prop, cfg->device) != hipSuccess) { free(h); return SV_EDEVICE; }
-    h->cus = prop.multiProcessorCount;
-    for (int v = 0; v < 2; ++v)
-        for (int g = 0; g < 2; ++g) {
-            const void* fn;
-            if (cfg->dtype == SV_BF16)
-                fn = v ? (g ? stream_fn<SV_BF16, true, true>() : stream_fn<SV_BF16, true, false>())
-                       : (g ? stream_fn<SV_BF16, false, true>() : stream_fn<SV_BF16, false, false>());
-            else
-                fn = v ? (g ? stream_fn<SV_F32, true, true>() : stream_fn<SV_F32, true, false>())
-                       : (g ? stream_fn<SV_F32, false, true>() : stream_fn<SV_F32, false, false>());
-            int n = 0;
-            if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, kThreads, 0) != hipSuccess || n < 1) n = 1;
-            h->occ[v][g] = n;
-        }
-
-    const long long ne = (long long)cfg->max_batch * (cfg->max_draft + 1);
+    const long long nrow = (long long)cfg->max_batch * (2 * cfg->max_draft + 1);
     const size_t ns = (size_t)h->nsplit;
     size_t off = 0;
     const size_t o_ctl = off; off = align_up(off + CTL_WORDS * sizeof(int));
-    const size_t o_q = off; off = align_up(off + ne * sizeof(uint32_t));
-    const size_t o_cnt = off; off = align_up(off + ne * sizeof(int));
-    const size_t o_pm = off; off = align_up(off + ne * 2 * ns * sizeof(float));
-    const size_t o_ps = off; off = align_up(off + ne * 2 * ns * sizeof(double));
-    const size_t o_pi = off; off = align_up(off + ne * ns * sizeof(int));
+    const size_t o_pm = off; off = align_up(off + nrow * ns * sizeof(float));
+    const size_t o_ps = off; off = align_up(off + nrow * ns * sizeof(double));
+    const size_t o_pi = off; off = align_up(off + nrow * ns * sizeof(int));
     const size_t o_st = off; off = align_up(off + (size_t)cfg->max_batch * sizeof(SeqState));
     const size_t o_rs = off; off = align_up(off + (size_t)cfg->max_batch * ns * sizeof(double));
     if (hipMalloc(&h->ws, off) != hipSuccess) { free(h); return SV_ENOMEM; }
     char* base = (char*)h->ws;
     h->w.ctl = (int*)(base + o_ctl);
-    h->w.queue = (uint32_t*)(base + o_q);
-    h->w.cnt = (int*)(base + o_cnt);
     h->w.part_m = (float*)(base + o_pm);
     h->w.part_s = (double*)(base + o_ps);
     h->w.part_i = (int*)(base + o_pi);
@@ -990,8 +971,9 @@ int spec_verify_destroy(spec_verify_t* h)
     if (!h) return SV_OK;
     DeviceGuard guard(h->cfg.device);
     if (h->ev) {
-        for (int i = 0; i < h->timing_max * K_COUNT * 2; ++i) (void)hipEventDestroy(h->ev[i]);
+        for (int i = 0; i < h->timing_max * kMaxSlots * 2; ++i) (void)hipEventDestroy(h->ev[i]);
         free(h->ev);
+        free(h->ev_kernel);
     }
     int rc = hipFree(h->ws) == hipSuccess ? SV_OK : SV_EDEVICE;
     free(h);
@@ -1000,16 +982,26 @@ int spec_verify_destroy(spec_verify_t* h)
 
 int spec_verify_timing_begin(spec_verify_t* h, int32_t max_calls)
 {
-    if (!h || max_calls < 1 || max_calls > 100000 || h->ev) return SV_EINVAL;
+    if (!h || max_calls < 1 || max_calls > 10000 || h->ev) return SV_EINVAL;
     DeviceGuard guard(h->cfg.device);
-    const int n = max_calls * K_COUNT * 2;
+    const int n = max_calls * kMaxSlots * 2;
     h->ev = (hipEvent_t*)calloc((size_t)n, sizeof(hipEvent_t));
-    if (!h->ev) return SV_ENOMEM;
+    h->ev_kernel = (int*)malloc(sizeof(int) * (size_t)max_calls * kMaxSlots);
+    if (!h->ev || !h->ev_kernel) {
+        free(h->ev);
+        free(h->ev_kernel);
+        h->ev = nullptr;
+        h->ev_kernel = nullptr;
+        return SV_ENOMEM;
+    }
+    for (int i = 0; i < max_calls * kMaxSlots; ++i) h->ev_kernel[i] = -1;
     for (int i = 0; i < n; ++i)
         if (hipEventCreate(&h->ev[i]) != hipSuccess) {
             for (int k = 0; k < i; ++k) (void)hipEventDestroy(h->ev[k]);
             free(h->ev);
+            free(h->ev_kernel);
             h->ev = nullptr;
+            h->ev_kernel = nullptr;
             return SV_EDEVICE;
         }
     h->timing_max = max_calls;
@@ -1024,19 +1016,23 @@ int spec_verify_timing_end(spec_verify_t* h, double* ms, int32_t n_kernels, int3
     int rc = SV_OK;
     for (int k = 0; k < n_kernels; ++k) ms[k] = 0.0;
     for (int c = 0; c < h->timing_n; ++c)
-        for (int k = 0; k < K_COUNT && k < n_kernels; ++k) {
-            hipEvent_t e0 = h->ev[(c * K_COUNT + k) * 2], e1 = h->ev[(c * K_COUNT + k) * 2 + 1];
+        for (int s = 0; s < kMaxSlots; ++s) {
+            const int k = h->ev_kernel[c * kMaxSlots + s];
+            if (k < 0) break;
+            hipEvent_t e0 = h->ev[(c * kMaxSlots + s) * 2], e1 = h->ev[(c * kMaxSlots + s) * 2 + 1];
             float t = 0.0f;
             if (hipEventSynchronize(e1) != hipSuccess || hipEventElapsedTime(&t, e0, e1) != hipSuccess) {
                 rc = SV_EDEVICE;
                 continue;
             }
-            ms[k] += t;
+            if (k < n_kernels) ms[k] += t;
         }
     if (n_runs) *n_runs = h->timing_n;
-    for (int i = 0; i < h->timing_max * K_COUNT * 2; ++i) (void)hipEventDestroy(h->ev[i]);
+    for (int i = 0; i < h->timing_max * kMaxSlots * 2; ++i) (void)hipEventDestroy(h->ev[i]);
     free(h->ev);
+    free(h->ev_kernel);
     h->ev = nullptr;
+    h->ev_kernel = nullptr;
     h->timing_max = h->timing_n = 0;
     return rc;
 }
@@ -1058,7 +1054,6 @@ int spec_verify_run(spec_verify_t* h, const spec_verify_args* a, void* hip_strea
     p.K = a->K;
     p.V = h->cfg.vocab;
     p.nsplit = h->nsplit;
-    p.ipe = greedy ? h->nsplit : 2 * h->nsplit;
     p.greedy = greedy;
     p.len_mode = a->length_mode;
     p.derived = (a->length_mode == SV_LEN_TAU && !a->confidence) ? 1 : 0;
@@ -1091,39 +1086,63 @@ int spec_verify_run(spec_verify_t* h, const spec_verify_args* a, void* hip_strea
     p.surv = a->survival;
     p.zmass = a->residual_mass;
     p.pys = a->sampled_prob;
+    p.rows_out = a->rows_read;
     p.status_out = a->device_status;
 
     const bool timing = h->ev && h->timing_n < h->timing_max;
+    int slot = 0;
     auto mark = [&](int k, int which) {
-        if (timing) (void)hipEventRecord(h->ev[(h->timing_n * K_COUNT + k) * 2 + which], s);
+        if (!timing || slot >= kMaxSlots) return;
+        const int idx = h->timing_n * kMaxSlots + slot;
+        (void)hipEventRecord(h->ev[idx * 2 + which], s);
+        if (which == 1) {
+            h->ev_kernel[idx] = k;
+            ++slot;
+        }
     };
-
-    const long long ne = (long long)p.B * (p.K + 1);
-    const long long items = ne * p.ipe;
     const int bf = h->cfg.dtype == SV_BF16;
+    const unsigned B = (unsigned)p.B;
 
     mark(K_PLAN, 0);
-    hipLaunchKernelGGL(sv_plan_kernel, dim3((unsigned)((ne + kThreads - 1) / kThreads)), dim3(kThreads), 0, s, p, h->w);
+    hipLaunchKernelGGL(sv_plan_kernel, dim3((B + kThreads - 1) / kThreads), dim3(kThreads), 0, s, p, h->w);
     mark(K_PLAN, 1);
 
-    long long grid = (long long)h->occ[vec][greedy] * h->cus;
-    if (grid > items) grid = items;
-    if (grid < 1) grid = 1;
-    mark(K_STREAM, 0);
-#define SV_STREAM(DT, VEC, G) hipLaunchKernelGGL((sv_stream_kernel<DT, VEC, G>), dim3((unsigned)grid), dim3(kThreads), 0, s, p, h->w)
-    if (bf) {
-        if (vec) { if (greedy) SV_STREAM(SV_BF16, true, true); else SV_STREAM(SV_BF16, true, false); }
-        else { if (greedy) SV_STREAM(SV_BF16, false, true); else SV_STREAM(SV_BF16, false, false); }
-    } else {
-        if (vec) { if (greedy) SV_STREAM(SV_F32, true, true); else SV_STREAM(SV_F32, true, false); }
-        else { if (greedy) SV_STREAM(SV_F32, false, true); else SV_STREAM(SV_F32, false, false); }
+    // groups of positions along the block: 2, 2, 4, 8, ... (a remainder of one
+    // position joins the previous group)
+    int j0 = 1, gsz = 2;
+    const int npos = p.K + 1;
+    while (j0 <= npos) {
+        int G = gsz;
+        if (npos - (j0 + G - 1) <= 1) G = npos - j0 + 1;
+        if (G > kMaxGroup) G = kMaxGroup;
+        const unsigned grid = B * (unsigned)(greedy ? G : 2 * G) * (unsigned)p.nsplit;
+        mark(K_ROWS, 0);
+#define SV_ROWS(DT, VEC, GR) hipLaunchKernelGGL((sv_rows_kernel<DT, VEC, GR>), dim3(grid), dim3(kThreads), 0, s, p, h->w, j0, G)
+        if (bf) {
+            if (vec) { if (greedy) SV_ROWS(SV_BF16, true, true); else SV_ROWS(SV_BF16, true, false); }
+            else { if (greedy) SV_ROWS(SV_BF16, false, true); else SV_ROWS(SV_BF16, false, false); }
+        } else {
+            if (vec) { if (greedy) SV_ROWS(SV_F32, true, true); else SV_ROWS(SV_F32, true, false); }
+            else { if (greedy) SV_ROWS(SV_F32, false, true); else SV_ROWS(SV_F32, false, false); }
+        }
+#undef SV_ROWS
+        mark(K_ROWS, 1);
+        mark(K_DECIDE, 0);
+        if (bf) {
+            if (greedy) hipLaunchKernelGGL((sv_decide_kernel<SV_BF16, true>), dim3(B), dim3(64), 0, s, p, h->w, j0, G);
+            else hipLaunchKernelGGL((sv_decide_kernel<SV_BF16, false>), dim3(B), dim3(64), 0, s, p, h->w, j0, G);
+        } else {
+            if (greedy) hipLaunchKernelGGL((sv_decide_kernel<SV_F32, true>), dim3(B), dim3(64), 0, s, p, h->w, j0, G);
+            else hipLaunchKernelGGL((sv_decide_kernel<SV_F32, false>), dim3(B), dim3(64), 0, s, p, h->w, j0, G);
+        }
+        mark(K_DECIDE, 1);
+        j0 += G;
+        gsz = gsz < kMaxGroup ? (j0 <= 3 ? 2 : gsz * 2) : kMaxGroup;
     }
-#undef SV_STREAM
-    mark(K_STREAM, 1);
 
     mark(K_RESID, 0);
     if (!greedy) {
-        const dim3 g((unsigned)((long long)p.B * p.nsplit));
+        const dim3 g(B * (unsigned)p.nsplit);
         if (bf) {
             if (vec) hipLaunchKernelGGL((sv_resid_kernel<SV_BF16, true>), g, dim3(kThreads), 0, s, p, h->w);
             else hipLaunchKernelGGL((sv_resid_kernel<SV_BF16, false>), g, dim3(kThreads), 0, s, p, h->w);
@@ -1135,8 +1154,13 @@ int spec_verify_run(spec_verify_t* h, const spec_verify_args* a, void* hip_strea
     mark(K_RESID, 1);
 
     mark(K_DRAW, 0);
-    if (bf) hipLaunchKernelGGL((sv_draw_kernel<SV_BF16>), dim3((unsigned)p.B), dim3(kThreads), 0, s, p, h->w);
-    else hipLaunchKernelGGL((sv_draw_kernel<SV_F32>), dim3((unsigned)p.B), dim3(kThreads), 0, s, p, h->w);
+    if (bf) {
+        if (vec) hipLaunchKernelGGL((sv_draw_kernel<SV_BF16, true>), dim3(B), dim3(kThreads), 0, s, p, h->w);
+        else hipLaunchKernelGGL((sv_draw_kernel<SV_BF16, false>), dim3(B), dim3(kThreads), 0, s, p, h->w);
+    } else {
+        if (vec) hipLaunchKernelGGL((sv_draw_kernel<SV_F32, true>), dim3(B), dim3(kThreads), 0, s, p, h->w);
+        else hipLaunchKernelGGL((sv_draw_kernel<SV_F32, false>), dim3(B), dim3(kThreads), 0, s, p, h->w);
+    }
     mark(K_DRAW, 1);
     if (timing) h->timing_n++;
 

@@ -50,6 +50,7 @@ class DeviceProblem:
     survival: Optional[torch.Tensor] = None
     residual_mass: Optional[torch.Tensor] = None
     sampled_prob: Optional[torch.Tensor] = None
+    rows_read: Optional[torch.Tensor] = None
     device_status: Optional[torch.Tensor] = None
 
     @staticmethod
@@ -81,6 +82,7 @@ class DeviceProblem:
         self.out_tokens = torch.full((Bn, K + 1), -7, **i32)
         self.verify_len_out = torch.full((Bn,), -7, **i32)
         self.device_status = torch.full((1,), -7, **i32)
+        self.rows_read = torch.full((Bn,), -7, **i32)
         if diagnostics:
             nan = float("nan")
             self.lse_target = torch.full((Bn, K + 1), nan, **f32)
@@ -96,13 +98,14 @@ class DeviceProblem:
             length_mode=self.length_mode, verify_len=self.verify_len, confidence=self.confidence, tau=self.tau,
             accepted_len=self.accepted_len, out_tokens=self.out_tokens, verify_len_out=self.verify_len_out,
             lse_target=self.lse_target, lse_draft=self.lse_draft, survival=self.survival,
-            residual_mass=self.residual_mass, sampled_prob=self.sampled_prob, device_status=self.device_status)
+            residual_mass=self.residual_mass, sampled_prob=self.sampled_prob, rows_read=self.rows_read,
+            device_status=self.device_status)
 
     def fetch(self) -> dict:
         torch.cuda.synchronize()
         out = {}
-        for name in ("accepted_len", "out_tokens", "verify_len_out", "device_status", "lse_target", "lse_draft",
-                     "survival", "residual_mass", "sampled_prob"):
+        for name in ("accepted_len", "out_tokens", "verify_len_out", "device_status", "rows_read", "lse_target",
+                     "lse_draft", "survival", "residual_mass", "sampled_prob"):
             t = getattr(self, name)
             out[name] = None if t is None else t.cpu().numpy()
         return out

@@ -60,6 +60,9 @@
  *                                 1 for a bonus draw; 0 if a rejection met Z <= 0
  *                                 (then the draw falls back to p); NaN for greedy
  *   sampled_prob   float [B]      probability of the final token under its draw
+ *   rows_read      int32 [B]      logit rows (target + draft) streamed for the
+ *                                 sequence; positions are walked in groups, so
+ *                                 rows after a rejection inside its group count
  *   device_status  int32 [1]      0, or SV_STATUS_* bits (see below)
  *
  * Ownership: the caller owns every buffer and keeps it alive until the work
@@ -99,7 +102,7 @@ enum { SV_STATUS_BAD_INPUT = 1, SV_STATUS_TIMEOUT = 2 };
 /* Limits checked by spec_verify_create. */
 #define SV_MAX_VOCAB 1048576
 #define SV_MAX_BATCH 1048575
-#define SV_MAX_DRAFT 1000
+#define SV_MAX_DRAFT 256
 
 typedef struct {
     int32_t max_batch; /* 1..SV_MAX_BATCH; workspace is sized from these three */
@@ -130,6 +133,7 @@ typedef struct {
     float* survival;               /* optional [B][K] */
     float* residual_mass;          /* optional [B] */
     float* sampled_prob;           /* optional [B] */
+    int32_t* rows_read;            /* optional [B] */
     int32_t* device_status;        /* optional [1] */
 } spec_verify_args;
 
