@@ -92,10 +92,11 @@ struct Work {
     int* part_i;      // same layout, split argmax (greedy)
     SeqState* st;     // [max_batch]
     double* rsum;     // [max_batch][nsplit] residual mass per split
+    double* seg;      // [max_batch][nsplit][64] residual mass per segment of a split
 };
 
 struct Params {
-    int B, K, V, nsplit;
+    int B, K, V, nsplit, seg_w;   // seg_w: the power of two >= nsplit
     int greedy, derived;       // derived: tau mode with c = max draft probability
     int len_mode;
     const void* t;
@@ -288,6 +289,30 @@ __device__ __forceinline__ float scaled_exp2(float l, float m, float c_hi, float
     return __builtin_amdgcn_exp2f(fmaf(t, c_hi, t * c_lo));
 }
 
+// 2^a in fp64: a = n + f with n = rint(a), |f| <= 1/2, and e^(f ln 2) from its
+// Taylor series to the x^11 term (|x| <= 0.347, truncation below 1e-14
+// relative), scaled by 2^n.  -inf and very negative a give 0; NaN passes.
+__device__ __forceinline__ double exp2_f64(double a)
+{
+    if (!(a > -1100.0)) return a != a ? a : 0.0;
+    if (a > 1100.0) return INFINITY;
+    const double n = rint(a);
+    const double x = (a - n) * 0.69314718055994530942;
+    double r = 2.505210838544171877505e-08;    // 1/11!
+    r = fma(r, x, 2.755731922398589065256e-07); // 1/10!
+    r = fma(r, x, 2.755731922398589065256e-06); // 1/9!
+    r = fma(r, x, 2.480158730158730158730e-05); // 1/8!
+    r = fma(r, x, 1.984126984126984126984e-04); // 1/7!
+    r = fma(r, x, 1.388888888888888888889e-03); // 1/6!
+    r = fma(r, x, 8.333333333333333333333e-03); // 1/5!
+    r = fma(r, x, 4.166666666666666666667e-02); // 1/4!
+    r = fma(r, x, 1.666666666666666666667e-01); // 1/3!
+    r = fma(r, x, 0.5);
+    r = fma(r, x, 1.0);
+    r = fma(r, x, 1.0);
+    return ldexp(r, (int)n);
+}
+
 // (max, sum exp) of one split: sum in fp32 over runs of 8 elements, fp64 beyond.
 template <int DT, bool VEC>
 __device__ void split_stats(const void* row, int V, int split, float c_hi, float c_lo, float& M, double& S,
@@ -442,61 +467,88 @@ __global__ __launch_bounds__(kThreads) void sv_rows_kernel(Params p, Work w, int
 
 // ---------------------------------------------------------------- sv_decide
 //
-// One wavefront per sequence.  Lanes merge the split partials of the group's
-// positions in parallel (fixed order, fp64) and gather the drafted tokens'
-// logits; lane 0 then walks the positions in order.
+// One workgroup per sequence.  Threads take (position, row, split) triples and
+// merge the split partials with fixed-order shuffles inside groups of sw lanes
+// (sw = the power of two >= nsplit), so every partial of the group is loaded in
+// one round trip; other threads gather the drafted tokens' logits.  Thread 0
+// then walks the positions in order.
+
+__device__ __forceinline__ float seg_max(float v, int sw)
+{
+    for (int o = sw >> 1; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+
+__device__ __forceinline__ double seg_sum(double v, int sw)
+{
+    for (int o = sw >> 1; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+__device__ __forceinline__ void seg_argmax(float& v, int& i, int sw)
+{
+    for (int o = sw >> 1; o > 0; o >>= 1) {
+        const float ov = __shfl_xor(v, o);
+        const int oi = __shfl_xor(i, o);
+        if (ov > v || (ov == v && oi < i)) { v = ov; i = oi; }
+    }
+}
 
 template <int DT, bool GREEDY>
-__global__ __launch_bounds__(64) void sv_decide_kernel(Params p, Work w, int j0, int G)
+__global__ __launch_bounds__(kThreads) void sv_decide_kernel(Params p, Work w, int j0, int G)
 {
     __shared__ float sMt[kMaxGroup], sMd[kMaxGroup], sLt[kMaxGroup], sLd[kMaxGroup];
     __shared__ double sSt[kMaxGroup], sSd[kMaxGroup];
     __shared__ int sG[kMaxGroup];
-    const int b = blockIdx.x, lane = threadIdx.x, K = p.K;
-    SeqState st = w.st[b];
-    bool acc = (st.flags & FL_ACC) != 0;
-    bool len = (st.flags & FL_LEN) != 0;
-    if (!acc && !len) return;
+    const int b = blockIdx.x, tid = threadIdx.x, K = p.K;
+    const int flags0 = w.st[b].flags, L0 = w.st[b].L;
+    if (!(flags0 & (FL_ACC | FL_LEN))) return;
     const int n = min(j0 + G - 1, K + 1) - j0 + 1;
-    const int flags0 = st.flags, L0 = st.L;
-
-    for (int pair = lane; pair < 2 * n; pair += 64) {
-        const int q = pair >> 1, kind = pair & 1, j = j0 + q;
-        const bool read = kind ? (!GREEDY && draft_row_needed(flags0, L0, j, K)) : target_row_needed(flags0, L0, j, K);
-        if (!read) continue;
-        const long long base = part_index(p, b, kind ? K + j : j - 1);
+    const int sw = p.seg_w;
+    const int per = 2 * n * sw;
+    for (int base = 0; base < per; base += kThreads) {
+        const int t = base + tid;
+        const int pk = t / sw, k = t % sw;
+        const int q = pk >> 1, kind = pk & 1, j = j0 + q;
+        const bool read = t < per && (kind ? (!GREEDY && draft_row_needed(flags0, L0, j, K))
+                                           : target_row_needed(flags0, L0, j, K));
+        const bool has = read && k < p.nsplit;
+        const long long pi = has ? part_index(p, b, kind ? K + j : j - 1) + k : 0;
         if (GREEDY) {
-            float bv = -INFINITY;
-            int bi = 0x7fffffff;
-            for (int k = 0; k < p.nsplit; ++k) {
-                const float v = w.part_m[base + k];
-                const int ix = w.part_i[base + k];
-                if (v > bv || (v == bv && ix < bi)) { bv = v; bi = ix; }
-            }
-            sMt[q] = bv;
-            sG[q] = bi;
+            float v = has ? w.part_m[pi] : -INFINITY;
+            int ix = has ? w.part_i[pi] : 0x7fffffff;
+            seg_argmax(v, ix, sw);
+            if (read && k == 0) { sMt[q] = v; sG[q] = ix; }
         } else {
-            float M = -INFINITY;
-            for (int k = 0; k < p.nsplit; ++k) M = fmaxf(M, w.part_m[base + k]);
-            double S = 0.0;
-            for (int k = 0; k < p.nsplit; ++k) {
-                const float m = w.part_m[base + k];
-                if (m != -INFINITY) S += w.part_s[base + k] * exp2(((double)m - (double)M) * p.c64);
+            const float m = has ? w.part_m[pi] : -INFINITY;
+            const double sv = has ? w.part_s[pi] : 0.0;
+            const float M = seg_max(m, sw);
+            double v = (has && m != -INFINITY) ? sv * exp2_f64(((double)m - (double)M) * p.c64) : 0.0;
+            v = seg_sum(v, sw);
+            if (read && k == 0) {
+                if (kind) { sMd[q] = M; sSd[q] = v; }
+                else { sMt[q] = M; sSt[q] = v; }
             }
-            if (kind) { sMd[q] = M; sSd[q] = S; }
-            else { sMt[q] = M; sSt[q] = S; }
-            if (j <= K) {
-                const int x = p.tok[(long long)b * K + (j - 1)];
-                if (x >= 0 && x < p.V) {
-                    if (kind) sLd[q] = load_one<DT>(row_ptr<DT>(p.d, p.dbs, p.drs, b, j - 1), x);
-                    else sLt[q] = load_one<DT>(row_ptr<DT>(p.t, p.tbs, p.trs, b, j - 1), x);
-                }
+        }
+    }
+    if (!GREEDY) {
+        // logits of the drafted tokens: threads 0..n-1 target rows, 64..64+n-1 draft rows
+        const int q = tid & 63, kind = tid >> 6, j = j0 + q;
+        if (kind < 2 && q < n && j <= K) {
+            const bool read = kind ? draft_row_needed(flags0, L0, j, K) : target_row_needed(flags0, L0, j, K);
+            const int x = p.tok[(long long)b * K + (j - 1)];
+            if (read && x >= 0 && x < p.V) {
+                if (kind) sLd[q] = load_one<DT>(row_ptr<DT>(p.d, p.dbs, p.drs, b, j - 1), x);
+                else sLt[q] = load_one<DT>(row_ptr<DT>(p.t, p.tbs, p.trs, b, j - 1), x);
             }
         }
     }
     __syncthreads();
-    if (lane != 0) return;
+    if (tid != 0) return;
 
+    SeqState st = w.st[b];
+    bool acc = (flags0 & FL_ACC) != 0;
+    bool len = (flags0 & FL_LEN) != 0;
     for (int q = 0; q < n; ++q) {
         const int j = j0 + q;
         const bool dread = !GREEDY && draft_row_needed(flags0, L0, j, K);
@@ -544,7 +596,7 @@ __global__ __launch_bounds__(64) void sv_decide_kernel(Params p, Work w, int j0,
                     ratio = INFINITY; // q(x) = 0
                 } else {
                     const double dlt = (double)lt - (double)sMt[q], dld = (double)ld - (double)sMd[q];
-                    ratio = exp2((dlt - dld) * p.c64) * (sSd[q] / sSt[q]);
+                    ratio = exp2_f64((dlt - dld) * p.c64) * (sSd[q] / sSt[q]);
                 }
                 const double uj = (double)p.u[(long long)b * (K + 1) + (j - 1)];
                 if (uj < ratio) {
@@ -574,10 +626,26 @@ __global__ __launch_bounds__(64) void sv_decide_kernel(Params p, Work w, int j0,
 }
 
 // ---------------------------------------------------------------- final draw
+//
+// Token order inside a split.  With the split layout above, load k of lane
+// (64 w + l) covers RUN consecutive tokens at split_base + (4k + w) SEG + l RUN,
+// where RUN = 8 (bf16) or 4 (fp32) and SEG = 64 RUN.  So the split is 4 NLOAD
+// consecutive segments of SEG tokens, segment g = 4k + w, and inside a segment
+// lane l holds tokens l RUN .. l RUN + RUN - 1.  The draw locates its token
+// split -> segment -> lane -> token, each level by a fixed-order prefix.
+
+template <int DT>
+struct Seg {
+    static constexpr int RUN = DT == SV_BF16 ? 8 : 4;
+    static constexpr int NLOAD = kPerLane / RUN;
+    static constexpr int SEGS = NLOAD * kWaves; // 32 (bf16) or 64 (fp32)
+    static constexpr int SEGLEN = 64 * RUN;
+};
+constexpr int kSegStride = 64; // segment sums stored per split
 
 struct DrawCtx {
     float Mt, Md, invSt, invSd, c_hi, c_lo;
-    double St, Sd, c64;
+    double iSt, iSd, c64;
 };
 
 __device__ __forceinline__ DrawCtx make_ctx(const SeqState& st, const Params& p)
@@ -585,10 +653,10 @@ __device__ __forceinline__ DrawCtx make_ctx(const SeqState& st, const Params& p)
     DrawCtx c;
     c.Mt = st.Mt;
     c.Md = st.Md;
-    c.St = st.St;
-    c.Sd = st.Sd;
-    c.invSt = (float)(1.0 / st.St);
-    c.invSd = st.Sd > 0.0 ? (float)(1.0 / st.Sd) : 0.0f;
+    c.iSt = 1.0 / st.St;
+    c.iSd = st.Sd > 0.0 ? 1.0 / st.Sd : 0.0;
+    c.invSt = (float)c.iSt;
+    c.invSd = (float)c.iSd;
     c.c_hi = p.c_hi;
     c.c_lo = p.c_lo;
     c.c64 = p.c64;
@@ -597,8 +665,8 @@ __device__ __forceinline__ DrawCtx make_ctx(const SeqState& st, const Params& p)
 
 __device__ __forceinline__ double mass_f64(float lt, float ld, const DrawCtx& c, bool resid)
 {
-    const double pd = exp2(((double)lt - (double)c.Mt) * c.c64) / c.St;
-    const double qd = resid ? exp2(((double)ld - (double)c.Md) * c.c64) / c.Sd : 0.0;
+    const double pd = exp2_f64(((double)lt - (double)c.Mt) * c.c64) * c.iSt;
+    const double qd = resid ? exp2_f64(((double)ld - (double)c.Md) * c.c64) * c.iSd : 0.0;
     return pd > qd ? pd - qd : 0.0;
 }
 
@@ -613,25 +681,6 @@ __device__ __forceinline__ double draw_mass(float lt, float ld, const DrawCtx& c
     return pf > qf ? (double)(pf - qf) : 0.0;
 }
 
-template <int DT, bool VEC>
-__global__ __launch_bounds__(kThreads) void sv_resid_kernel(Params p, Work w)
-{
-    __shared__ double redd[kWaves];
-    const int b = (int)(blockIdx.x / p.nsplit);
-    const int split = (int)(blockIdx.x % p.nsplit);
-    if (w.st[b].kind != KIND_RESID) return;
-    const SeqState st = w.st[b];
-    const DrawCtx c = make_ctx(st, p);
-    Chunk<DT> tc, dc;
-    tc.template load<VEC>(row_ptr<DT>(p.t, p.tbs, p.trs, b, st.js - 1), split * kSplit, p.V, threadIdx.x);
-    dc.template load<VEC>(row_ptr<DT>(p.d, p.dbs, p.drs, b, st.js - 1), split * kSplit, p.V, threadIdx.x);
-    double acc = 0.0;
-#pragma unroll
-    for (int e = 0; e < kPerLane; ++e) acc += draw_mass(tc.get(e), dc.get(e), c, true);
-    acc = block_sum(acc, redd);
-    if (threadIdx.x == 0) w.rsum[(long long)b * p.nsplit + split] = acc;
-}
-
 // Inclusive prefix sum over the 64 lanes of a wavefront (fixed order).
 __device__ __forceinline__ double wave_incl_scan(double v, int lane)
 {
@@ -643,51 +692,80 @@ __device__ __forceinline__ double wave_incl_scan(double v, int lane)
     return v;
 }
 
-// 64 consecutive elements of a row starting at i0 (thread-contiguous layout).
-template <int DT, bool VEC>
-struct Run {
-    float v[64];
-    __device__ __forceinline__ void load(const void* row, int i0, int V)
-    {
-        if (DT == SV_BF16) {
-            const uint16_t* r = (const uint16_t*)row;
+// Segment sums of one split (all 256 threads): lane run sums of RUN tokens,
+// scanned across each wavefront; lane 63 holds the segment total.
+template <int DT>
+__device__ __forceinline__ void split_segments(const Chunk<DT>& tc, const Chunk<DT>& dc, const DrawCtx& c, bool resid,
+                                               double* seg_out)
+{
+    using S = Seg<DT>;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const int i = i0 + 8 * k;
-                if (VEC && i < V) {
-                    const uint4 q = *(const uint4*)(r + i);
-                    const uint32_t ws[4] = {q.x, q.y, q.z, q.w};
+    for (int k = 0; k < S::NLOAD; ++k) {
+        double r = 0.0;
 #pragma unroll
-                    for (int h = 0; h < 4; ++h) { v[8 * k + 2 * h] = bf16_lo(ws[h]); v[8 * k + 2 * h + 1] = bf16_hi(ws[h]); }
-                } else {
-#pragma unroll
-                    for (int h = 0; h < 8; ++h) v[8 * k + h] = (i + h < V) ? bf16_lo((uint32_t)r[i + h]) : -INFINITY;
-                }
-            }
-        } else {
-            const float* r = (const float*)row;
-#pragma unroll
-            for (int k = 0; k < 16; ++k) {
-                const int i = i0 + 4 * k;
-                if (VEC && i < V) {
-                    const float4 q = *(const float4*)(r + i);
-                    v[4 * k] = q.x; v[4 * k + 1] = q.y; v[4 * k + 2] = q.z; v[4 * k + 3] = q.w;
-                } else {
-#pragma unroll
-                    for (int h = 0; h < 4; ++h) v[4 * k + h] = (i + h < V) ? r[i + h] : -INFINITY;
-                }
-            }
-        }
+        for (int i = 0; i < S::RUN; ++i)
+            r += draw_mass(tc.get(k * S::RUN + i), resid ? dc.get(k * S::RUN + i) : 0.0f, c, resid);
+        const double incl = wave_incl_scan(r, lane);
+        if (lane == 63) seg_out[k * kWaves + wv] = incl;
     }
-};
+}
+
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kThreads) void sv_resid_kernel(Params p, Work w)
+{
+    using S = Seg<DT>;
+    __shared__ double s_seg[S::SEGS];
+    const int b = (int)(blockIdx.x / p.nsplit);
+    const int split = (int)(blockIdx.x % p.nsplit);
+    if (w.st[b].kind != KIND_RESID) return;
+    const SeqState st = w.st[b];
+    const DrawCtx c = make_ctx(st, p);
+    Chunk<DT> tc, dc;
+    tc.template load<VEC>(row_ptr<DT>(p.t, p.tbs, p.trs, b, st.js - 1), split * kSplit, p.V, threadIdx.x);
+    dc.template load<VEC>(row_ptr<DT>(p.d, p.dbs, p.drs, b, st.js - 1), split * kSplit, p.V, threadIdx.x);
+    split_segments<DT>(tc, dc, c, true, s_seg);
+    __syncthreads();
+    const long long so = ((long long)b * p.nsplit + split) * kSegStride;
+    if (threadIdx.x < S::SEGS) w.seg[so + threadIdx.x] = s_seg[threadIdx.x];
+    if (threadIdx.x == 0) {
+        double tot = 0.0;
+        for (int g = 0; g < S::SEGS; ++g) tot += s_seg[g];
+        w.rsum[(long long)b * p.nsplit + split] = tot;
+    }
+}
+
+// First lane whose inclusive prefix exceeds w (lanes < n), as (lane, w minus
+// the exclusive prefix of that lane); lane -1 if none.  All lanes take part.
+__device__ __forceinline__ int wave_select(double v, int n, double target, double& rel)
+{
+    const int lane = threadIdx.x & 63;
+    const double incl = wave_incl_scan(v, lane);
+    const double up = __shfl_up(incl, 1); // every lane takes part in the shuffle
+    const double excl = lane == 0 ? 0.0 : up;
+    const unsigned long long pass = __ballot(lane < n && incl > target);
+    if (!pass) { rel = INFINITY; return -1; }
+    const int f = __ffsll(pass) - 1;
+    rel = target - __shfl(excl, f);
+    return f;
+}
+
+// Last lane (< n) with v > 0, or -1.
+__device__ __forceinline__ int wave_last_positive(double v, int n)
+{
+    const int lane = threadIdx.x & 63;
+    const unsigned long long pos = __ballot(lane < n && v > 0.0);
+    return pos ? 63 - __clzll(pos) : -1;
+}
 
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kThreads) void sv_draw_kernel(Params p, Work w)
 {
-    __shared__ double s_wtot[kWaves];
+    using S = Seg<DT>;
+    __shared__ double s_seg[S::SEGS];
     __shared__ double s_wrel, s_Z, s_my;
-    __shared__ int s_split, s_resid, s_first[kWaves], s_lastpos[kWaves], s_y;
-    const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    __shared__ int s_split, s_resid, s_y;
+    const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
     const int K = p.K;
     const SeqState st = w.st[b];
     int kind = st.kind;
@@ -696,35 +774,25 @@ __global__ __launch_bounds__(kThreads) void sv_draw_kernel(Params p, Work w)
     float zrep = NAN, py = NAN;
 
     if (kind == KIND_RESID || kind == KIND_BONUS) {
-        // 1. masses of the splits and the split that holds the draw point (wave 0)
-        if (wv == 0) {
+        // 1. the split holding the draw point (wave 0, lane k = split k)
+        if (tid < 64) {
             bool resid = kind == KIND_RESID;
             double m = (resid && lane < p.nsplit) ? w.rsum[(long long)b * p.nsplit + lane] : 0.0;
-            double incl = wave_incl_scan(m, lane);
-            const double Z = __shfl(incl, p.nsplit - 1);
+            const double Z = __shfl(wave_incl_scan(m, lane), p.nsplit - 1);
             if (resid && !(Z > 0.0)) resid = false; // cannot happen in exact arithmetic after a rejection
             if (!resid) {
                 m = 0.0;
                 if (lane < p.nsplit) {
                     const long long pb = part_index(p, b, st.js - 1) + lane;
                     const float mk = w.part_m[pb];
-                    if (mk != -INFINITY) m = w.part_s[pb] * exp2(((double)mk - (double)st.Mt) * p.c64) / st.St;
+                    if (mk != -INFINITY) m = w.part_s[pb] * exp2_f64(((double)mk - (double)st.Mt) * p.c64) / st.St;
                 }
-                incl = wave_incl_scan(m, lane);
             }
             const double uf = (double)p.u[(long long)b * (K + 1) + K];
-            const double target = resid ? uf * Z : uf;
-            const double up = __shfl_up(incl, 1); // every lane takes part in the shuffle
-            const double excl = lane == 0 ? 0.0 : up;
-            const unsigned long long pass = __ballot(lane < p.nsplit && incl > target);
-            int ks;
             double wrel;
-            if (pass) {
-                ks = __ffsll(pass) - 1;
-                wrel = target - __shfl(excl, ks);
-            } else { // rounding: the last split with mass, its last token
-                const unsigned long long pos = __ballot(lane < p.nsplit && m > 0.0);
-                ks = pos ? 63 - __clzll(pos) : 0;
+            int ks = wave_select(m, p.nsplit, resid ? uf * Z : uf, wrel);
+            if (ks < 0) { // rounding: the last split with mass, its last token
+                ks = max(wave_last_positive(m, p.nsplit), 0);
                 wrel = INFINITY;
             }
             if (lane == 0) {
@@ -736,62 +804,65 @@ __global__ __launch_bounds__(kThreads) void sv_draw_kernel(Params p, Work w)
         }
         __syncthreads();
         const bool resid = s_resid != 0;
+        const int ks = s_split;
         const DrawCtx c = make_ctx(st, p);
         const void* trow = row_ptr<DT>(p.t, p.tbs, p.trs, b, st.js - 1);
         const void* drow = resid ? row_ptr<DT>(p.d, p.dbs, p.drs, b, st.js - 1) : nullptr;
-        const int i0 = s_split * kSplit + tid * 64;
-        const double wrel = s_wrel;
 
-        // 2. thread sums over 64 consecutive tokens, then a fixed-order block scan
-        Run<DT, VEC> tr, dr;
-        tr.load(trow, i0, p.V);
-        if (resid) dr.load(drow, i0, p.V);
-        double s = 0.0;
-        int last_pos = -1;
-#pragma unroll
-        for (int e = 0; e < 64; ++e) {
-            const double mv = draw_mass(tr.v[e], resid ? dr.v[e] : 0.0f, c, resid);
-            s += mv;
-            if (mv > 0.0) last_pos = i0 + e;
-        }
-        const double incl = wave_incl_scan(s, lane);
-        if (lane == 63) s_wtot[wv] = incl;
-        __syncthreads();
-        double woff = 0.0;
-        for (int k = 0; k < wv; ++k) woff += s_wtot[k];
-        const double up = __shfl_up(incl, 1); // every lane takes part in the shuffle
-        const double prefix = woff + (lane == 0 ? 0.0 : up);
-        const unsigned long long pass = __ballot(prefix + s > wrel);
-        const unsigned long long pos = __ballot(s > 0.0);
-        if (lane == 0) {
-            s_first[wv] = pass ? wv * 64 + __ffsll(pass) - 1 : 0x7fffffff;
-            s_lastpos[wv] = pos ? wv * 64 + 63 - __clzll(pos) : -1;
+        // 2. segment sums of that split: stored by sv_resid for a replacement,
+        //    computed here for a bonus draw
+        if (resid) {
+            if (tid < S::SEGS) s_seg[tid] = w.seg[((long long)b * p.nsplit + ks) * kSegStride + tid];
+        } else {
+            Chunk<DT> tc;
+            tc.template load<VEC>(trow, ks * kSplit, p.V, tid);
+            split_segments<DT>(tc, tc, c, false, s_seg);
         }
         __syncthreads();
-        int tstar = 0x7fffffff, tlast = -1;
-        for (int k = 0; k < kWaves; ++k) {
-            tstar = min(tstar, s_first[k]);
-            tlast = max(tlast, s_lastpos[k]);
-        }
-        const bool fallback = wrel == INFINITY || tstar == 0x7fffffff;
-        if (fallback) tstar = tlast >= 0 ? tlast : 0;
 
-        // 3. the thread that holds the crossing walks its tokens in order
-        if (tid == tstar) {
-            int yy = -1;
-            if (!fallback) {
-                double cl = 0.0;
-#pragma unroll
-                for (int e = 0; e < 64; ++e) {
-                    const double mv = draw_mass(tr.v[e], resid ? dr.v[e] : 0.0f, c, resid);
-                    cl += mv;
-                    if (yy < 0 && prefix + cl > wrel) yy = i0 + e;
-                }
+        // 3. segment, lane and token (wave 0)
+        if (tid < 64) {
+            const double wrel = s_wrel;
+            double wseg = INFINITY;
+            int g = wrel == INFINITY ? -1 : wave_select(lane < S::SEGS ? s_seg[lane] : 0.0, S::SEGS, wrel, wseg);
+            if (g < 0) {
+                g = max(wave_last_positive(lane < S::SEGS ? s_seg[lane] : 0.0, S::SEGS), 0);
+                wseg = INFINITY;
             }
-            if (yy < 0) yy = last_pos >= 0 ? last_pos : i0;
-            s_y = yy;
-            // the reported probability of the chosen token is evaluated in fp64
-            s_my = mass_f64(load_one<DT>(trow, yy), resid ? load_one<DT>(drow, yy) : 0.0f, c, resid);
+            const int i0 = ks * kSplit + g * S::SEGLEN + lane * S::RUN;
+            float lt[S::RUN], ld[S::RUN];
+#pragma unroll
+            for (int i = 0; i < S::RUN; ++i) {
+                lt[i] = i0 + i < p.V ? load_one<DT>(trow, i0 + i) : -INFINITY;
+                ld[i] = (resid && i0 + i < p.V) ? load_one<DT>(drow, i0 + i) : -INFINITY;
+            }
+            double m[S::RUN], r = 0.0;
+            int lastpos = -1;
+#pragma unroll
+            for (int i = 0; i < S::RUN; ++i) {
+                m[i] = draw_mass(lt[i], ld[i], c, resid);
+                r += m[i];
+                if (m[i] > 0.0) lastpos = i0 + i;
+            }
+            double wl;
+            int l = wseg == INFINITY ? -1 : wave_select(r, 64, wseg, wl);
+            bool walk = l >= 0;
+            if (!walk) l = max(wave_last_positive(r, 64), 0);
+            if (lane == l) {
+                int yy = -1;
+                if (walk) {
+                    double cl = 0.0;
+#pragma unroll
+                    for (int i = 0; i < S::RUN; ++i) {
+                        cl += m[i];
+                        if (yy < 0 && cl > wl) yy = i0 + i;
+                    }
+                }
+                if (yy < 0) yy = lastpos >= 0 ? lastpos : i0; // rounding: last token with mass
+                s_y = yy;
+                // the reported probability of the chosen token is evaluated in fp64
+                s_my = mass_f64(load_one<DT>(trow, yy), resid ? load_one<DT>(drow, yy) : 0.0f, c, resid);
+            }
         }
         __syncthreads();
         y = s_y;
@@ -954,6 +1025,7 @@ int spec_verify_create(const spec_verify_config* cfg, spec_verify_t** out)
     const size_t o_pi = off; off = align_up(off + nrow * ns * sizeof(int));
     const size_t o_st = off; off = align_up(off + (size_t)cfg->max_batch * sizeof(SeqState));
     const size_t o_rs = off; off = align_up(off + (size_t)cfg->max_batch * ns * sizeof(double));
+    const size_t o_sg = off; off = align_up(off + (size_t)cfg->max_batch * ns * kSegStride * sizeof(double));
     if (hipMalloc(&h->ws, off) != hipSuccess) { free(h); return SV_ENOMEM; }
     char* base = (char*)h->ws;
     h->w.ctl = (int*)(base + o_ctl);
@@ -962,6 +1034,7 @@ int spec_verify_create(const spec_verify_config* cfg, spec_verify_t** out)
     h->w.part_i = (int*)(base + o_pi);
     h->w.st = (SeqState*)(base + o_st);
     h->w.rsum = (double*)(base + o_rs);
+    h->w.seg = (double*)(base + o_sg);
     *out = h;
     return SV_OK;
 }
@@ -1054,6 +1127,8 @@ int spec_verify_run(spec_verify_t* h, const spec_verify_args* a, void* hip_strea
     p.K = a->K;
     p.V = h->cfg.vocab;
     p.nsplit = h->nsplit;
+    p.seg_w = 1;
+    while (p.seg_w < p.nsplit) p.seg_w <<= 1;
     p.greedy = greedy;
     p.len_mode = a->length_mode;
     p.derived = (a->length_mode == SV_LEN_TAU && !a->confidence) ? 1 : 0;
@@ -1129,11 +1204,11 @@ int spec_verify_run(spec_verify_t* h, const spec_verify_args* a, void* hip_strea
         mark(K_ROWS, 1);
         mark(K_DECIDE, 0);
         if (bf) {
-            if (greedy) hipLaunchKernelGGL((sv_decide_kernel<SV_BF16, true>), dim3(B), dim3(64), 0, s, p, h->w, j0, G);
-            else hipLaunchKernelGGL((sv_decide_kernel<SV_BF16, false>), dim3(B), dim3(64), 0, s, p, h->w, j0, G);
+            if (greedy) hipLaunchKernelGGL((sv_decide_kernel<SV_BF16, true>), dim3(B), dim3(kThreads), 0, s, p, h->w, j0, G);
+            else hipLaunchKernelGGL((sv_decide_kernel<SV_BF16, false>), dim3(B), dim3(kThreads), 0, s, p, h->w, j0, G);
         } else {
-            if (greedy) hipLaunchKernelGGL((sv_decide_kernel<SV_F32, true>), dim3(B), dim3(64), 0, s, p, h->w, j0, G);
-            else hipLaunchKernelGGL((sv_decide_kernel<SV_F32, false>), dim3(B), dim3(64), 0, s, p, h->w, j0, G);
+            if (greedy) hipLaunchKernelGGL((sv_decide_kernel<SV_F32, true>), dim3(B), dim3(kThreads), 0, s, p, h->w, j0, G);
+            else hipLaunchKernelGGL((sv_decide_kernel<SV_F32, false>), dim3(B), dim3(kThreads), 0, s, p, h->w, j0, G);
         }
         mark(K_DECIDE, 1);
         j0 += G;
