@@ -1,0 +1,126 @@
+"""The C ABI on the host: the library loads without a GPU, exports every symbol
+include/spec_verify.h declares, and rejects bad arguments before any device
+work (spec_verify_check is host-only).  No compute call is made here."""
+import ast
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "spec_verify.h")
+
+
+@pytest.fixture(scope="module")
+def B():
+    from draft_verification_amd import binding, build
+    if not os.path.exists(binding.LIB_PATH):
+        build.build()
+    return binding
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b(spec_verify_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("spec_verify_create", "spec_verify_run", "spec_verify_destroy", "spec_verify_check"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(B):
+    L = B.lib()
+    for n in declared_functions():
+        assert hasattr(L, n), n
+    assert set(B.EXPORTED) == set(declared_functions())
+
+
+def test_status_strings_and_kernel_names(B):
+    assert B.status_string(B.SV_OK) == "ok"
+    assert "invalid" in B.status_string(B.SV_EINVAL)
+    assert B.status_string(12345) == "unknown status"
+    names = B.kernel_names()
+    assert names == ["sv_plan", "sv_rows", "sv_decide", "sv_resid", "sv_draw"]
+    assert B.lib().spec_verify_kernel_name(99) == b""
+
+
+def _valid(B, T=1.0, mode=None, K=4, Bn=3):
+    cfg = B.Config(8, 8, 1000, B.SV_BF16, 0)
+    fake = 1 << 40  # an address that is never dereferenced: checks are host-only
+    a = B.make_args(Bn, K, target=fake, draft=fake, tokens=fake, uniforms=fake, temperature=T,
+                    target_strides=((K + 1) * 1000, 1000), draft_strides=(K * 1000, 1000),
+                    length_mode=B.SV_LEN_FIXED if mode is None else mode, tau=fake,
+                    accepted_len=fake, out_tokens=fake, verify_len_out=fake)
+    return cfg, a
+
+
+def test_check_accepts_valid_arguments(B):
+    cfg, a = _valid(B)
+    assert B.check(cfg, a) == B.SV_OK
+    cfg, a = _valid(B, mode=B.SV_LEN_TAU)
+    assert B.check(cfg, a) == B.SV_OK
+
+
+@pytest.mark.parametrize("field,value", [
+    ("B", -1), ("B", 9), ("K", 0), ("K", 9), ("temperature", -0.5), ("temperature", float("nan")),
+    ("temperature", float("inf")), ("length_mode", 7), ("target_logits", None), ("draft_tokens", None),
+    ("target_row_stride", 999), ("target_batch_stride", -1), ("draft_logits", None), ("uniforms", None),
+    ("draft_row_stride", 10), ("accepted_len", None), ("out_tokens", None), ("verify_len_out", None),
+])
+def test_check_rejects(B, field, value):
+    cfg, a = _valid(B)
+    setattr(a, field, value)
+    assert B.check(cfg, a) == B.SV_EINVAL
+
+
+def test_greedy_needs_no_draft_but_tau_needs_a_confidence(B):
+    cfg, a = _valid(B, T=0.0)
+    a.draft_logits = None
+    a.uniforms = None
+    assert B.check(cfg, a) == B.SV_OK
+    a.length_mode = B.SV_LEN_TAU
+    assert B.check(cfg, a) == B.SV_EINVAL      # c = max q needs T > 0
+    a.confidence = 1 << 40
+    assert B.check(cfg, a) == B.SV_OK
+    a.tau = None
+    assert B.check(cfg, a) == B.SV_EINVAL
+
+
+def test_empty_batch_is_valid(B):
+    cfg, a = _valid(B, Bn=0)
+    a.target_logits = None
+    assert B.check(cfg, a) == B.SV_OK
+
+
+@pytest.mark.parametrize("cfg", [(0, 4, 100, 1, 0), (4, 0, 100, 1, 0), (4, 4, 0, 1, 0), (4, 4, 100, 7, 0),
+                                 (4, 4, 100, 1, -1), (4, 257, 100, 1, 0), (4, 4, 2 ** 20 + 1, 1, 0)])
+def test_bad_configs_are_rejected_before_device_work(B, cfg):
+    c = B.Config(*cfg)
+    a = B.Args()
+    assert B.check(c, a) in (B.SV_EINVAL, B.SV_EUNSUPPORTED)
+    h = ctypes.c_void_p()
+    assert B.lib().spec_verify_create(ctypes.byref(c), ctypes.byref(h)) in (B.SV_EINVAL, B.SV_EUNSUPPORTED)
+    assert not h.value
+
+
+def test_destroy_null_is_a_no_op(B):
+    assert B.lib().spec_verify_destroy(None) == B.SV_OK
+
+
+def test_product_package_never_imports_the_oracle():
+    pkg = os.path.join(ROOT, "draft_verification_amd")
+    for fn in os.listdir(pkg):
+        if not fn.endswith(".py"):
+            continue
+        tree = ast.parse(open(os.path.join(pkg, fn)).read())
+        for node in ast.walk(tree):
+            if isinstance(node, ast.Import):
+                assert not any("oracle" in a.name for a in node.names), fn
+            if isinstance(node, ast.ImportFrom):
+                assert "oracle" not in (node.module or ""), fn
+    src = open(os.path.join(pkg, "csrc", "spec_verify.hip")).read()
+    assert "sv_oracle" not in src and "svo_" not in src
