@@ -53,6 +53,7 @@
 
 #include <math.h>
 #include <stdint.h>
+#include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -93,6 +94,7 @@ struct Work {
     SeqState* st;     // [max_batch]
     double* rsum;     // [max_batch][nsplit] residual mass per split
     double* seg;      // [max_batch][nsplit][64] residual mass per segment of a split
+    float* xlog;      // [max_batch][2K+1] logit of the drafted token in each row
 };
 
 struct Params {
@@ -156,14 +158,23 @@ __device__ __forceinline__ void wave_argmax(float& v, int& i)
     }
 }
 
+// Workgroup barrier that orders LDS only: global loads issued before it may
+// stay in flight (so the next split can be prefetched across a reduction).
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __device__ __forceinline__ float block_max(float v, float* red)
 {
     v = wave_max(v);
     const int w = threadIdx.x >> 6;
     if ((threadIdx.x & 63) == 0) red[w] = v;
-    __syncthreads();
+    lds_barrier();
     float r = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    __syncthreads();
+    lds_barrier();
     return r;
 }
 
@@ -172,9 +183,9 @@ __device__ __forceinline__ double block_sum(double v, double* red)
     v = wave_sum(v);
     const int w = threadIdx.x >> 6;
     if ((threadIdx.x & 63) == 0) red[w] = v;
-    __syncthreads();
+    lds_barrier();
     double r = ((red[0] + red[1]) + red[2]) + red[3];
-    __syncthreads();
+    lds_barrier();
     return r;
 }
 
@@ -183,13 +194,13 @@ __device__ __forceinline__ void block_argmax(float& v, int& i, float* redf, int*
     wave_argmax(v, i);
     const int w = threadIdx.x >> 6;
     if ((threadIdx.x & 63) == 0) { redf[w] = v; redi[w] = i; }
-    __syncthreads();
+    lds_barrier();
     v = redf[0];
     i = redi[0];
 #pragma unroll
     for (int k = 1; k < kWaves; ++k)
         if (redf[k] > v || (redf[k] == v && redi[k] < i)) { v = redf[k]; i = redi[k]; }
-    __syncthreads();
+    lds_barrier();
 }
 
 // ---------------------------------------------------------------- split loads
@@ -313,13 +324,11 @@ __device__ __forceinline__ double exp2_f64(double a)
     return ldexp(r, (int)n);
 }
 
-// (max, sum exp) of one split: sum in fp32 over runs of 8 elements, fp64 beyond.
-template <int DT, bool VEC>
-__device__ void split_stats(const void* row, int V, int split, float c_hi, float c_lo, float& M, double& S,
-                            float* redf, double* redd)
+// (max, sum exp) of one loaded split: sum in fp32 over runs of 8 elements, fp64 beyond.
+template <int DT>
+__device__ __forceinline__ void chunk_stats(const Chunk<DT>& c, float c_hi, float c_lo, float& M, double& S,
+                                            float* redf, double* redd)
 {
-    Chunk<DT> c;
-    c.template load<VEC>(row, split * kSplit, V, threadIdx.x);
     float m = -INFINITY;
 #pragma unroll
     for (int e = 0; e < kPerLane; ++e) m = fmaxf(m, c.get(e));
@@ -338,12 +347,11 @@ __device__ void split_stats(const void* row, int V, int split, float c_hi, float
     M = m;
 }
 
-// (max, lowest index of the max) of one split of the raw row.
-template <int DT, bool VEC>
-__device__ void split_argmax(const void* row, int V, int split, float& M, int& I, float* redf, int* redi)
+// (max, lowest index of the max) of one loaded split of the raw row.
+template <int DT>
+__device__ __forceinline__ void chunk_argmax(const Chunk<DT>& c, int V, int split, float& M, int& I, float* redf,
+                                             int* redi)
 {
-    Chunk<DT> c;
-    c.template load<VEC>(row, split * kSplit, V, threadIdx.x);
     float best = -INFINITY;
     int bi = 0x7fffffff;
 #pragma unroll
@@ -427,14 +435,15 @@ __device__ __forceinline__ bool draft_row_needed(int flags, int L, int j, int K)
     return j <= K && ((flags & FL_LEN) || ((flags & FL_ACC) && j <= L));
 }
 
-template <int DT, bool VEC, bool GREEDY>
+template <int DT, bool VEC, bool GREEDY, int SPW>
 __global__ __launch_bounds__(kThreads) void sv_rows_kernel(Params p, Work w, int j0, int G)
 {
     __shared__ float redf[kWaves];
     __shared__ double redd[kWaves];
     __shared__ int redi[kWaves];
-    const int split = (int)(blockIdx.x % p.nsplit);
-    const int rest = (int)(blockIdx.x / p.nsplit);
+    const int nchunk = (p.nsplit + SPW - 1) / SPW;
+    const int chunk = (int)(blockIdx.x % nchunk);
+    const int rest = (int)(blockIdx.x / nchunk);
     const int slots = GREEDY ? G : 2 * G;
     const int slot = rest % slots;
     const int b = rest / slots;
@@ -445,22 +454,37 @@ __global__ __launch_bounds__(kThreads) void sv_rows_kernel(Params p, Work w, int
     const bool need = draft ? draft_row_needed(flags, L, j, p.K) : target_row_needed(flags, L, j, p.K);
     if (!need) return;
     const void* row = draft ? row_ptr<DT>(p.d, p.dbs, p.drs, b, j - 1) : row_ptr<DT>(p.t, p.tbs, p.trs, b, j - 1);
-    const long long pi = part_index(p, b, draft ? p.K + j : j - 1) + split;
-    if (GREEDY) {
-        float M;
-        int I;
-        split_argmax<DT, VEC>(row, p.V, split, M, I, redf, redi);
-        if (threadIdx.x == 0) {
-            w.part_m[pi] = M;
-            w.part_i[pi] = I;
-        }
-    } else {
-        float M;
-        double S;
-        split_stats<DT, VEC>(row, p.V, split, p.c_hi, p.c_lo, M, S, redf, redd);
-        if (threadIdx.x == 0) {
-            w.part_m[pi] = M;
-            w.part_s[pi] = S;
+    const int prow = draft ? p.K + j : j - 1;
+    const long long pbase = part_index(p, b, prow);
+    const int s0 = chunk * SPW;
+    // drafted token of this position: the workgroup whose splits hold it keeps its logit
+    const int x = (!GREEDY && threadIdx.x == 0 && j <= p.K) ? p.tok[(long long)b * p.K + (j - 1)] : -1;
+    Chunk<DT> c[2];
+    c[0].template load<VEC>(row, s0 * kSplit, p.V, threadIdx.x);
+#pragma unroll
+    for (int i = 0; i < SPW; ++i) {
+        const int split = s0 + i;
+        if (split >= p.nsplit) break;
+        if (i + 1 < SPW && split + 1 < p.nsplit) // prefetch the next split before reducing this one
+            c[(i + 1) & 1].template load<VEC>(row, (split + 1) * kSplit, p.V, threadIdx.x);
+        if (GREEDY) {
+            float M;
+            int I;
+            chunk_argmax<DT>(c[i & 1], p.V, split, M, I, redf, redi);
+            if (threadIdx.x == 0) {
+                w.part_m[pbase + split] = M;
+                w.part_i[pbase + split] = I;
+            }
+        } else {
+            float M;
+            double S;
+            chunk_stats<DT>(c[i & 1], p.c_hi, p.c_lo, M, S, redf, redd);
+            if (threadIdx.x == 0) {
+                w.part_m[pbase + split] = M;
+                w.part_s[pbase + split] = S;
+                if (x >= split * kSplit && x < (split + 1) * kSplit && x < p.V)
+                    w.xlog[(long long)b * (2 * p.K + 1) + prow] = load_one<DT>(row, x);
+            }
         }
     }
 }
@@ -500,6 +524,8 @@ __global__ __launch_bounds__(kThreads) void sv_decide_kernel(Params p, Work w, i
     __shared__ float sMt[kMaxGroup], sMd[kMaxGroup], sLt[kMaxGroup], sLd[kMaxGroup];
     __shared__ double sSt[kMaxGroup], sSd[kMaxGroup];
     __shared__ int sG[kMaxGroup];
+    __shared__ double sRatio[kMaxGroup];
+    __shared__ float sLseT[kMaxGroup], sLseD[kMaxGroup];
     const int b = blockIdx.x, tid = threadIdx.x, K = p.K;
     const int flags0 = w.st[b].flags, L0 = w.st[b].L;
     if (!(flags0 & (FL_ACC | FL_LEN))) return;
@@ -532,15 +558,36 @@ __global__ __launch_bounds__(kThreads) void sv_decide_kernel(Params p, Work w, i
         }
     }
     if (!GREEDY) {
-        // logits of the drafted tokens: threads 0..n-1 target rows, 64..64+n-1 draft rows
+        // logits of the drafted tokens, kept by sv_rows: threads 0..n-1 target rows, 64..64+n-1 draft rows
         const int q = tid & 63, kind = tid >> 6, j = j0 + q;
         if (kind < 2 && q < n && j <= K) {
             const bool read = kind ? draft_row_needed(flags0, L0, j, K) : target_row_needed(flags0, L0, j, K);
-            const int x = p.tok[(long long)b * K + (j - 1)];
-            if (read && x >= 0 && x < p.V) {
-                if (kind) sLd[q] = load_one<DT>(row_ptr<DT>(p.d, p.dbs, p.drs, b, j - 1), x);
-                else sLt[q] = load_one<DT>(row_ptr<DT>(p.t, p.tbs, p.trs, b, j - 1), x);
+            if (read) {
+                const float v = w.xlog[(long long)b * (2 * K + 1) + (kind ? K + j : j - 1)];
+                if (kind) sLd[q] = v;
+                else sLt[q] = v;
             }
+        }
+    }
+    __syncthreads();
+    if (!GREEDY) {
+        // per-position quantities in parallel: the acceptance ratio p(x)/q(x), and the
+        // rows' log-sum-exp when asked for (thread q handles position j0 + q)
+        const int q = tid, j = j0 + q;
+        if (q < n) {
+            const bool tread = target_row_needed(flags0, L0, j, K);
+            const bool dread = draft_row_needed(flags0, L0, j, K);
+            if (tread && dread) {
+                const float ld = sLd[q];
+                double ratio = INFINITY; // q(x) = 0
+                if (ld != -INFINITY) {
+                    const double dlt = (double)sLt[q] - (double)sMt[q], dld = (double)ld - (double)sMd[q];
+                    ratio = exp2_f64((dlt - dld) * p.c64) * (sSd[q] / sSt[q]);
+                }
+                sRatio[q] = ratio;
+            }
+            if (tread && p.lse_t) sLseT[q] = (float)((double)sMt[q] * p.invT64 + log(sSt[q]));
+            if (dread && p.lse_d) sLseD[q] = (float)((double)sMd[q] * p.invT64 + log(sSd[q]));
         }
     }
     __syncthreads();
@@ -555,8 +602,8 @@ __global__ __launch_bounds__(kThreads) void sv_decide_kernel(Params p, Work w, i
         st.rows += (target_row_needed(flags0, L0, j, K) ? 1 : 0) + (dread ? 1 : 0);
         if (!acc && !len) continue; // rows of this group past the stop were still streamed
         if (!GREEDY) {
-            if (acc && p.lse_t) p.lse_t[(long long)b * (K + 1) + (j - 1)] = (float)((double)sMt[q] * p.invT64 + log(sSt[q]));
-            if (dread && p.lse_d) p.lse_d[(long long)b * K + (j - 1)] = (float)((double)sMd[q] * p.invT64 + log(sSd[q]));
+            if (acc && p.lse_t) p.lse_t[(long long)b * (K + 1) + (j - 1)] = sLseT[q];
+            if (dread && p.lse_d) p.lse_d[(long long)b * K + (j - 1)] = sLseD[q];
             if (dread && p.derived) {
                 // c_j = max_v q_j(v) = 1 / Sd; S_j = S_{j-1} c_j
                 const double S = st.S / sSd[q];
@@ -590,14 +637,7 @@ __global__ __launch_bounds__(kThreads) void sv_decide_kernel(Params p, Work w, i
                     acc = false;
                 }
             } else {
-                const float lt = sLt[q], ld = sLd[q];
-                double ratio;
-                if (ld == -INFINITY) {
-                    ratio = INFINITY; // q(x) = 0
-                } else {
-                    const double dlt = (double)lt - (double)sMt[q], dld = (double)ld - (double)sMd[q];
-                    ratio = exp2_f64((dlt - dld) * p.c64) * (sSd[q] / sSt[q]);
-                }
+                const double ratio = sRatio[q];
                 const double uj = (double)p.u[(long long)b * (K + 1) + (j - 1)];
                 if (uj < ratio) {
                     st.a = j;
@@ -671,13 +711,14 @@ __device__ __forceinline__ double mass_f64(float lt, float ld, const DrawCtx& c,
 }
 
 // Mass of one token under the final draw: max(0, p - q) for a replacement,
-// p for a bonus.  fp32 first; masses whose p or q exceeds 2^-12 are evaluated
-// in fp64 (at most 2^13 tokens of a row pair qualify).
+// p for a bonus.  fp32 first; masses whose p or q exceeds 2^-9 are evaluated
+// in fp64 (at most 2^10 tokens of a row pair qualify).  Below that, the fp32
+// value carries < 2e-7 relative error, so the CDF error stays below 1e-8.
 __device__ __forceinline__ double draw_mass(float lt, float ld, const DrawCtx& c, bool resid)
 {
     const float pf = scaled_exp2(lt, c.Mt, c.c_hi, c.c_lo) * c.invSt;
     const float qf = resid ? scaled_exp2(ld, c.Md, c.c_hi, c.c_lo) * c.invSd : 0.0f;
-    if (fmaxf(pf, qf) > 0x1p-12f) return mass_f64(lt, ld, c, resid);
+    if (fmaxf(pf, qf) > 0x1p-9f) return mass_f64(lt, ld, c, resid);
     return pf > qf ? (double)(pf - qf) : 0.0;
 }
 
@@ -692,6 +733,37 @@ __device__ __forceinline__ double wave_incl_scan(double v, int lane)
     return v;
 }
 
+// Mass of a run of RUN consecutive tokens, in token order.  The fast path is
+// branch-free fp32 per token, summed in fp64; a run that holds a token whose p
+// or q exceeds 2^-9 is summed again with draw_mass (fp64 for those tokens).
+// Both kernels that need a run's mass call this, so the sums agree bit for bit.
+template <int RUN>
+__device__ __forceinline__ double run_mass(const float (&lt)[RUN], const float (&ld)[RUN], const DrawCtx& c, bool resid,
+                                           bool& slow)
+{
+    double acc = 0.0;
+    bool big = false;
+#pragma unroll
+    for (int i = 0; i < RUN; ++i) {
+        const float pf = scaled_exp2(lt[i], c.Mt, c.c_hi, c.c_lo) * c.invSt;
+        const float qf = resid ? scaled_exp2(ld[i], c.Md, c.c_hi, c.c_lo) * c.invSd : 0.0f;
+        big |= fmaxf(pf, qf) > 0x1p-9f;
+        acc += (double)(pf > qf ? pf - qf : 0.0f);
+    }
+    slow = big;
+    return acc;
+}
+
+template <int RUN>
+__device__ __forceinline__ double run_mass_exact(const float (&lt)[RUN], const float (&ld)[RUN], const DrawCtx& c,
+                                                 bool resid)
+{
+    double acc = 0.0;
+#pragma unroll
+    for (int i = 0; i < RUN; ++i) acc += draw_mass(lt[i], ld[i], c, resid);
+    return acc;
+}
+
 // Segment sums of one split (all 256 threads): lane run sums of RUN tokens,
 // scanned across each wavefront; lane 63 holds the segment total.
 template <int DT>
@@ -702,10 +774,15 @@ __device__ __forceinline__ void split_segments(const Chunk<DT>& tc, const Chunk<
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
 #pragma unroll
     for (int k = 0; k < S::NLOAD; ++k) {
-        double r = 0.0;
+        float lt[S::RUN], ld[S::RUN];
 #pragma unroll
-        for (int i = 0; i < S::RUN; ++i)
-            r += draw_mass(tc.get(k * S::RUN + i), resid ? dc.get(k * S::RUN + i) : 0.0f, c, resid);
+        for (int i = 0; i < S::RUN; ++i) {
+            lt[i] = tc.get(k * S::RUN + i);
+            ld[i] = resid ? dc.get(k * S::RUN + i) : 0.0f;
+        }
+        bool slow;
+        double r = run_mass<S::RUN>(lt, ld, c, resid, slow);
+        if (slow) r = run_mass_exact<S::RUN>(lt, ld, c, resid); // rare: a large p or q in the run
         const double incl = wave_incl_scan(r, lane);
         if (lane == 63) seg_out[k * kWaves + wv] = incl;
     }
@@ -836,12 +913,21 @@ __global__ __launch_bounds__(kThreads) void sv_draw_kernel(Params p, Work w)
                 lt[i] = i0 + i < p.V ? load_one<DT>(trow, i0 + i) : -INFINITY;
                 ld[i] = (resid && i0 + i < p.V) ? load_one<DT>(drow, i0 + i) : -INFINITY;
             }
-            double m[S::RUN], r = 0.0;
+            bool slow;
+            double r = run_mass<S::RUN>(lt, ld, c, resid, slow);
+            if (slow) r = run_mass_exact<S::RUN>(lt, ld, c, resid);
+            // per-token masses with the same arithmetic as the run sum, for the walk
+            double m[S::RUN];
             int lastpos = -1;
 #pragma unroll
             for (int i = 0; i < S::RUN; ++i) {
-                m[i] = draw_mass(lt[i], ld[i], c, resid);
-                r += m[i];
+                if (slow) {
+                    m[i] = draw_mass(lt[i], ld[i], c, resid);
+                } else {
+                    const float pf = scaled_exp2(lt[i], c.Mt, c.c_hi, c.c_lo) * c.invSt;
+                    const float qf = resid ? scaled_exp2(ld[i], c.Md, c.c_hi, c.c_lo) * c.invSd : 0.0f;
+                    m[i] = (double)(pf > qf ? pf - qf : 0.0f);
+                }
                 if (m[i] > 0.0) lastpos = i0 + i;
             }
             double wl;
@@ -901,6 +987,7 @@ constexpr int kMaxSlots = 64; // timed launches per run
 struct spec_verify {
     spec_verify_config cfg;
     int nsplit;
+    int spw_sched[4];     // splits per sv_rows workgroup for groups 0, 1, 2, >= 3
     void* ws;
     Work w;
     int timing_max, timing_n;
@@ -1016,6 +1103,12 @@ int spec_verify_create(const spec_verify_config* cfg, spec_verify_t** out)
     if (!h) return SV_ENOMEM;
     h->cfg = *cfg;
     h->nsplit = nsplit_of(cfg->vocab);
+    {
+        const int def[4] = {1, 1, 2, 4};
+        for (int i = 0; i < 4; ++i) h->spw_sched[i] = def[i];
+        if (const char* e = getenv("SV_SPW_EXPERIMENT"))
+            sscanf(e, "%d,%d,%d,%d", &h->spw_sched[0], &h->spw_sched[1], &h->spw_sched[2], &h->spw_sched[3]);
+    }
     const long long nrow = (long long)cfg->max_batch * (2 * cfg->max_draft + 1);
     const size_t ns = (size_t)h->nsplit;
     size_t off = 0;
@@ -1026,6 +1119,7 @@ int spec_verify_create(const spec_verify_config* cfg, spec_verify_t** out)
     const size_t o_st = off; off = align_up(off + (size_t)cfg->max_batch * sizeof(SeqState));
     const size_t o_rs = off; off = align_up(off + (size_t)cfg->max_batch * ns * sizeof(double));
     const size_t o_sg = off; off = align_up(off + (size_t)cfg->max_batch * ns * kSegStride * sizeof(double));
+    const size_t o_xl = off; off = align_up(off + nrow * sizeof(float));
     if (hipMalloc(&h->ws, off) != hipSuccess) { free(h); return SV_ENOMEM; }
     char* base = (char*)h->ws;
     h->w.ctl = (int*)(base + o_ctl);
@@ -1035,6 +1129,7 @@ int spec_verify_create(const spec_verify_config* cfg, spec_verify_t** out)
     h->w.st = (SeqState*)(base + o_st);
     h->w.rsum = (double*)(base + o_rs);
     h->w.seg = (double*)(base + o_sg);
+    h->w.xlog = (float*)(base + o_xl);
     *out = h;
     return SV_OK;
 }
@@ -1184,22 +1279,27 @@ int spec_verify_run(spec_verify_t* h, const spec_verify_args* a, void* hip_strea
 
     // groups of positions along the block: 2, 2, 4, 8, ... (a remainder of one
     // position joins the previous group)
-    int j0 = 1, gsz = 2;
+    int j0 = 1, gsz = 2, gidx = 0;
     const int npos = p.K + 1;
     while (j0 <= npos) {
         int G = gsz;
         if (npos - (j0 + G - 1) <= 1) G = npos - j0 + 1;
         if (G > kMaxGroup) G = kMaxGroup;
-        const unsigned grid = B * (unsigned)(greedy ? G : 2 * G) * (unsigned)p.nsplit;
+        int spw = gidx < 4 ? h->spw_sched[gidx] : h->spw_sched[3];
+        if (spw > p.nsplit) spw = p.nsplit >= 4 ? 4 : (p.nsplit >= 2 ? 2 : 1);
+        const unsigned nchunk = (unsigned)((p.nsplit + spw - 1) / spw);
+        const unsigned grid = B * (unsigned)(greedy ? G : 2 * G) * nchunk;
         mark(K_ROWS, 0);
-#define SV_ROWS(DT, VEC, GR) hipLaunchKernelGGL((sv_rows_kernel<DT, VEC, GR>), dim3(grid), dim3(kThreads), 0, s, p, h->w, j0, G)
+#define SV_ROWS(DT, VEC, GR, W) hipLaunchKernelGGL((sv_rows_kernel<DT, VEC, GR, W>), dim3(grid), dim3(kThreads), 0, s, p, h->w, j0, G)
+#define SV_ROWS_SPW(DT, VEC, GR) do { if (spw >= 4) SV_ROWS(DT, VEC, GR, 4); else if (spw == 2) SV_ROWS(DT, VEC, GR, 2); else SV_ROWS(DT, VEC, GR, 1); } while (0)
         if (bf) {
-            if (vec) { if (greedy) SV_ROWS(SV_BF16, true, true); else SV_ROWS(SV_BF16, true, false); }
-            else { if (greedy) SV_ROWS(SV_BF16, false, true); else SV_ROWS(SV_BF16, false, false); }
+            if (vec) { if (greedy) SV_ROWS_SPW(SV_BF16, true, true); else SV_ROWS_SPW(SV_BF16, true, false); }
+            else { if (greedy) SV_ROWS_SPW(SV_BF16, false, true); else SV_ROWS_SPW(SV_BF16, false, false); }
         } else {
-            if (vec) { if (greedy) SV_ROWS(SV_F32, true, true); else SV_ROWS(SV_F32, true, false); }
-            else { if (greedy) SV_ROWS(SV_F32, false, true); else SV_ROWS(SV_F32, false, false); }
+            if (vec) { if (greedy) SV_ROWS_SPW(SV_F32, true, true); else SV_ROWS_SPW(SV_F32, true, false); }
+            else { if (greedy) SV_ROWS_SPW(SV_F32, false, true); else SV_ROWS_SPW(SV_F32, false, false); }
         }
+#undef SV_ROWS_SPW
 #undef SV_ROWS
         mark(K_ROWS, 1);
         mark(K_DECIDE, 0);
@@ -1212,6 +1312,7 @@ int spec_verify_run(spec_verify_t* h, const spec_verify_args* a, void* hip_strea
         }
         mark(K_DECIDE, 1);
         j0 += G;
+        ++gidx;
         gsz = gsz < kMaxGroup ? (j0 <= 3 ? 2 : gsz * 2) : kMaxGroup;
     }
 
