@@ -111,28 +111,27 @@ static inline double load_logit(const void* base, int dtype, int64_t idx)
     return (double)((const float*)base)[idx];
 }
 
-/* log-sum-exp of z = l / T over one row: lse = m + ln sum exp(z - m). */
-static double row_lse(const void* base, int dtype, int64_t off, int32_t V, double T)
+/* softmax of z = l / T over one row, kept as (m, s): m = max z,
+ * s = sum exp(z - m), so that softmax(z)_v = exp(z_v - m) / s and
+ * lse = m + ln s.  Probabilities are formed against m, never against lse:
+ * z_v - lse in fp64 loses ln s once |z| is large (1e30 and ln 20000 round to
+ * the same double), while z_v - m is exact there. */
+typedef struct { double m, s; } svo_softmax;
+
+static svo_softmax row_softmax(const void* base, int dtype, int64_t off, int32_t V, double T)
 {
-    double m = -INFINITY;
+    svo_softmax r = {-INFINITY, 0.0};
     for (int32_t v = 0; v < V; ++v) {
         double z = load_logit(base, dtype, off + v) / T;
-        if (z > m) m = z;
+        if (z > r.m) r.m = z;
     }
-    double s = 0.0;
-    for (int32_t v = 0; v < V; ++v) s += exp(load_logit(base, dtype, off + v) / T - m);
-    return m + log(s);
+    for (int32_t v = 0; v < V; ++v) r.s += exp(load_logit(base, dtype, off + v) / T - r.m);
+    return r;
 }
 
-/* max_v softmax(l/T)_v of one row. */
-static double row_max_prob(const void* base, int dtype, int64_t off, int32_t V, double T, double lse)
+static inline double softmax_at(svo_softmax r, const void* base, int dtype, int64_t idx, double T)
 {
-    double m = -INFINITY;
-    for (int32_t v = 0; v < V; ++v) {
-        double z = load_logit(base, dtype, off + v) / T;
-        if (z > m) m = z;
-    }
-    return exp(m - lse);
+    return exp(load_logit(base, dtype, idx) / T - r.m) / r.s;
 }
 
 /* Argmax of the raw row, lowest index on ties. */
@@ -197,6 +196,14 @@ static void verify_one(const svo_problem* P, int32_t b, int32_t i, const svo_res
 
     for (int32_t j = 0; j <= K; ++j) { out[j] = -1; lse_t[j] = NAN; }
     for (int32_t j = 0; j < K; ++j) { lse_d[j] = NAN; surv[j] = NAN; }
+    /* softmax of every row the step reads, computed once (lse_* NaN = not yet) */
+    svo_softmax sm_t[K + 1], sm_d[K > 0 ? K : 1];
+#define NEED_T(j) do { if (isnan(lse_t[(j) - 1])) { \
+        sm_t[(j) - 1] = row_softmax(P->target, P->dtype, tb + (int64_t)((j) - 1) * P->target_row_stride, V, T); \
+        lse_t[(j) - 1] = sm_t[(j) - 1].m + log(sm_t[(j) - 1].s); } } while (0)
+#define NEED_D(j) do { if (isnan(lse_d[(j) - 1])) { \
+        sm_d[(j) - 1] = row_softmax(P->draft, P->dtype, db + (int64_t)((j) - 1) * P->draft_row_stride, V, T); \
+        lse_d[(j) - 1] = sm_d[(j) - 1].m + log(sm_d[(j) - 1].s); } } while (0)
     int32_t margin = 0;
     double accept_gap = INFINITY, cdf_gap = INFINITY;
     int32_t alt = -1;
@@ -227,9 +234,8 @@ static void verify_one(const svo_problem* P, int32_t b, int32_t i, const svo_res
             if (P->confidence) {
                 c = (double)P->confidence[(int64_t)b * K + (j - 1)];
             } else {
-                const int64_t off = db + (int64_t)(j - 1) * P->draft_row_stride;
-                lse_d[j - 1] = row_lse(P->draft, P->dtype, off, V, T);
-                c = row_max_prob(P->draft, P->dtype, off, V, T, lse_d[j - 1]);
+                NEED_D(j);
+                c = 1.0 / sm_d[j - 1].s; /* max_v q_j(v) = exp(m - m) / s */
             }
             S *= c;
             surv[j - 1] = S;
@@ -266,12 +272,12 @@ static void verify_one(const svo_problem* P, int32_t b, int32_t i, const svo_res
         for (int32_t j = 1; j <= L; ++j) {
             const int64_t toff = tb + (int64_t)(j - 1) * P->target_row_stride;
             const int64_t doff = db + (int64_t)(j - 1) * P->draft_row_stride;
-            if (isnan(lse_t[j - 1])) lse_t[j - 1] = row_lse(P->target, P->dtype, toff, V, T);
-            if (isnan(lse_d[j - 1])) lse_d[j - 1] = row_lse(P->draft, P->dtype, doff, V, T);
+            NEED_T(j);
+            NEED_D(j);
             const int32_t xj = x[j - 1];
             if (xj < 0 || xj >= V) { bad = 1; break; }
-            const double p = exp(load_logit(P->target, P->dtype, toff + xj) / T - lse_t[j - 1]);
-            const double q = exp(load_logit(P->draft, P->dtype, doff + xj) / T - lse_d[j - 1]);
+            const double p = softmax_at(sm_t[j - 1], P->target, P->dtype, toff + xj, T);
+            const double q = softmax_at(sm_d[j - 1], P->draft, P->dtype, doff + xj, T);
             const double ratio = q > 0.0 ? p / q : INFINITY;
             const double uj = (double)u[j - 1];
             const double gap = fabs(uj - ratio);
@@ -289,7 +295,7 @@ static void verify_one(const svo_problem* P, int32_t b, int32_t i, const svo_res
         } else {
             const int32_t js = a + 1; /* the row of the final draw (1-based) */
             const int64_t toff = tb + (int64_t)(js - 1) * P->target_row_stride;
-            if (isnan(lse_t[js - 1])) lse_t[js - 1] = row_lse(P->target, P->dtype, toff, V, T);
+            NEED_T(js);
             const double uf = (double)u[K];
             int use_p = !rejected;
             if (rejected) {
@@ -297,8 +303,8 @@ static void verify_one(const svo_problem* P, int32_t b, int32_t i, const svo_res
                 const int64_t doff = db + (int64_t)(js - 1) * P->draft_row_stride;
                 double Zr = 0.0;
                 for (int32_t v = 0; v < V; ++v) {
-                    const double p = exp(load_logit(P->target, P->dtype, toff + v) / T - lse_t[js - 1]);
-                    const double q = exp(load_logit(P->draft, P->dtype, doff + v) / T - lse_d[js - 1]);
+                    const double p = softmax_at(sm_t[js - 1], P->target, P->dtype, toff + v, T);
+                    const double q = softmax_at(sm_d[js - 1], P->draft, P->dtype, doff + v, T);
                     r[v] = p > q ? p - q : 0.0;
                     Zr += r[v];
                 }
@@ -318,7 +324,7 @@ static void verify_one(const svo_problem* P, int32_t b, int32_t i, const svo_res
             if (use_p) {
                 /* bonus (or the degenerate replacement): draw from p of that row, w = u */
                 for (int32_t v = 0; v < V; ++v)
-                    r[v] = exp(load_logit(P->target, P->dtype, toff + v) / T - lse_t[js - 1]);
+                    r[v] = softmax_at(sm_t[js - 1], P->target, P->dtype, toff + v, T);
                 y = inverse_cdf(r, V, uf, 1.0, &cdf_gap, &alt);
                 py = r[y];
             }
@@ -327,13 +333,9 @@ static void verify_one(const svo_problem* P, int32_t b, int32_t i, const svo_res
     }
 
     if (P->all_rows && !greedy) {
-        for (int32_t j = 1; j <= K + 1; ++j)
-            if (isnan(lse_t[j - 1]))
-                lse_t[j - 1] = row_lse(P->target, P->dtype, tb + (int64_t)(j - 1) * P->target_row_stride, V, T);
+        for (int32_t j = 1; j <= K + 1; ++j) NEED_T(j);
         if (P->draft)
-            for (int32_t j = 1; j <= K; ++j)
-                if (isnan(lse_d[j - 1]))
-                    lse_d[j - 1] = row_lse(P->draft, P->dtype, db + (int64_t)(j - 1) * P->draft_row_stride, V, T);
+            for (int32_t j = 1; j <= K; ++j) NEED_D(j);
     }
 
     /* ---- emit: accepted prefix, then the final token ---- */
@@ -350,6 +352,8 @@ static void verify_one(const svo_problem* P, int32_t b, int32_t i, const svo_res
     R->accept_gap[i] = accept_gap;
     R->cdf_gap[i] = cdf_gap;
     R->alt_token[i] = alt;
+#undef NEED_T
+#undef NEED_D
 }
 
 /* Returns 0, or -1 for arguments the definition does not cover. */

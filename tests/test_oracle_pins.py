@@ -250,6 +250,51 @@ def test_bonus_on_bf16_rows_at_temperature():
         assert r.out_tokens[b, 0] == int(np.searchsorted(np.cumsum(p), np.float64(u[b, K]), side="right"))
 
 
+@pytest.mark.parametrize("offset", [1.0e30, -1.0e30, 3.0e38])
+def test_huge_equal_logits_give_the_uniform_distribution(offset):
+    # every logit equal (the noise is below one ulp of the offset): p = q = 1/V,
+    # so every verified position is accepted (ratio 1), the bonus token is the
+    # inverse CDF of the uniform distribution, floor(u * V), with probability 1/V,
+    # and lse = offset / T + ln V
+    rng = _rng(21)
+    B, K, V = 16, 3, 1000
+    t = (np.float32(offset) + rng.standard_normal((B, K + 1, V)).astype(np.float32)).astype(np.float32)
+    d = (np.float32(offset) + rng.standard_normal((B, K, V)).astype(np.float32)).astype(np.float32)
+    assert np.all(t == np.float32(offset)) and np.all(d == np.float32(offset))
+    tok = rng.integers(0, V, size=(B, K), dtype=np.int32)
+    u = rng.random((B, K + 1)).astype(np.float32)
+    r = O.verify(t, d, tok, u, 1.0, dtype=F32, all_rows=True)
+    assert np.all(r.accepted_len == K)
+    for b in range(B):
+        if r.margin[b] & O.MARGIN_CDF:
+            continue
+        assert r.out_tokens[b, K] == int(np.floor(np.float64(u[b, K]) * V))
+        np.testing.assert_allclose(r.sampled_prob[b], 1.0 / V, rtol=1e-12)
+    np.testing.assert_allclose(r.lse_target, np.float64(np.float32(offset)) + np.log(V), rtol=1e-15)
+
+
+def test_bonus_draw_is_shift_invariant_at_large_offsets():
+    # softmax does not change when a constant is added to the row; with an
+    # offset of 2^20 and logits on a 2^-3 grid every value stays exact in fp32,
+    # so the draw and its probability equal scipy's softmax of the unshifted row
+    rng = _rng(22)
+    B, K, V = 200, 1, 700
+    base = (np.round(8 * 2.0 * rng.standard_normal((B, K + 1, V))) / 8).astype(np.float32)
+    t = (base + np.float32(2 ** 20)).astype(np.float32)
+    assert np.array_equal(t.astype(np.float64) - 2 ** 20, base.astype(np.float64))
+    d = t[:, :K].copy()
+    tok = rng.integers(0, V, size=(B, K), dtype=np.int32)
+    u = rng.random((B, K + 1)).astype(np.float32)
+    r = O.verify(t, d, tok, u, 1.0, dtype=F32, verify_len=np.zeros(B, np.int32))
+    for b in range(B):
+        if r.margin[b] & O.MARGIN_CDF:
+            continue
+        p = special.softmax(base[b, 0].astype(np.float64))
+        y = int(np.searchsorted(np.cumsum(p), np.float64(u[b, K]), side="right"))
+        assert r.out_tokens[b, 0] == y
+        np.testing.assert_allclose(r.sampled_prob[b], p[y], rtol=1e-12)
+
+
 # ------------------------------------------------------------ greedy ----
 
 def test_greedy_prefix_and_argmax():
