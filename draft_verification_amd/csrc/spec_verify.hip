@@ -89,9 +89,11 @@ struct SeqState {
 struct Work {
     int* ctl;
     float* part_m;    // [B][2K+1][nsplit] split maxima; row j-1 target, K+j draft (j 1-based)
-    double* part_s;   // same layout, split sums of exp2((l - m) c)
+    double* part_s;   // same layout, split sums of exp2((l - m) c + d)
+    float* part_d;    // same layout, the d of that sum (the true split sum is part_s * 2^-d)
     int* part_i;      // same layout, split argmax (greedy)
     SeqState* st;     // [max_batch]
+    int* live;        // [max_batch] (L + 1) << 2 | flags, the part of st that sv_rows reads
     double* rsum;     // [max_batch][nsplit] residual mass per split
     double* seg;      // [max_batch][nsplit][64] residual mass per segment of a split
     float* xlog;      // [max_batch][2K+1] logit of the drafted token in each row
@@ -112,6 +114,7 @@ struct Params {
     const float* tau;
     double invT64, c64;        // 1/T and log2(e)/T in fp64
     float c_hi, c_lo;          // c64 = c_hi + c_lo, c_hi rounded toward zero, c_lo > 0
+    float c32;                 // c64 rounded to nearest
     int* acc_out;
     int* out_tok;
     int* vl_out;
@@ -167,33 +170,34 @@ __device__ __forceinline__ void lds_barrier()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-__device__ __forceinline__ float block_max(float v, float* red)
+// Workgroup reductions over kThreads threads; t is the thread's index.
+__device__ __forceinline__ float block_max(float v, float* red, int t = threadIdx.x)
 {
     v = wave_max(v);
-    const int w = threadIdx.x >> 6;
-    if ((threadIdx.x & 63) == 0) red[w] = v;
+    const int w = t >> 6;
+    if ((t & 63) == 0) red[w] = v;
     lds_barrier();
     float r = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
     lds_barrier();
     return r;
 }
 
-__device__ __forceinline__ double block_sum(double v, double* red)
+__device__ __forceinline__ double block_sum(double v, double* red, int t = threadIdx.x)
 {
     v = wave_sum(v);
-    const int w = threadIdx.x >> 6;
-    if ((threadIdx.x & 63) == 0) red[w] = v;
+    const int w = t >> 6;
+    if ((t & 63) == 0) red[w] = v;
     lds_barrier();
     double r = ((red[0] + red[1]) + red[2]) + red[3];
     lds_barrier();
     return r;
 }
 
-__device__ __forceinline__ void block_argmax(float& v, int& i, float* redf, int* redi)
+__device__ __forceinline__ void block_argmax(float& v, int& i, float* redf, int* redi, int t = threadIdx.x)
 {
     wave_argmax(v, i);
-    const int w = threadIdx.x >> 6;
-    if ((threadIdx.x & 63) == 0) { redf[w] = v; redi[w] = i; }
+    const int w = t >> 6;
+    if ((t & 63) == 0) { redf[w] = v; redi[w] = i; }
     lds_barrier();
     v = redf[0];
     i = redi[0];
@@ -224,6 +228,8 @@ struct Chunk<SV_BF16> {
     uint32_t w[kPerLane / 2];
     __device__ __forceinline__ float get(int e) const { return (e & 1) ? bf16_hi(w[e >> 1]) : bf16_lo(w[e >> 1]); }
     __device__ __forceinline__ static int index(int base, int lane, int e) { return base + (e >> 3) * 2048 + lane * 8 + (e & 7); }
+    // lane and element holding offset off (0 <= off < kSplit) of the split
+    __device__ __forceinline__ static void owner(int off, int& lane, int& e) { lane = (off >> 3) & 255; e = (off >> 11) * 8 + (off & 7); }
     template <bool VEC>
     __device__ __forceinline__ void load(const void* row, int base, int V, int lane)
     {
@@ -249,6 +255,33 @@ struct Chunk<SV_BF16> {
             }
         }
     }
+    // Same data as load(), with every vector load issued unconditionally (the
+    // address of a vector past V is clamped to the row's last vector) so that
+    // the number of loads in flight is fixed and a later chunk's loads need not
+    // be waited for; fix_tail() then sets the vectors past V to -inf.
+    template <bool VEC>
+    __device__ __forceinline__ void issue(const void* row, int base, int V, int lane)
+    {
+        if (!VEC) {
+            load<false>(row, base, V, lane);
+            return;
+        }
+        const uint16_t* r = (const uint16_t*)row;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int i0 = base + k * 2048 + lane * 8;
+            const uint4 q = *(const uint4*)(r + (i0 < V ? i0 : V - 8));
+            w[4 * k] = q.x; w[4 * k + 1] = q.y; w[4 * k + 2] = q.z; w[4 * k + 3] = q.w;
+        }
+    }
+    template <bool VEC>
+    __device__ __forceinline__ void fix_tail(int base, int V, int lane)
+    {
+        if (!VEC || base + kSplit <= V) return;
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            if (base + k * 2048 + lane * 8 >= V) w[4 * k] = w[4 * k + 1] = w[4 * k + 2] = w[4 * k + 3] = 0xFF80FF80u;
+    }
 };
 
 template <>
@@ -256,6 +289,7 @@ struct Chunk<SV_F32> {
     float w[kPerLane];
     __device__ __forceinline__ float get(int e) const { return w[e]; }
     __device__ __forceinline__ static int index(int base, int lane, int e) { return base + (e >> 2) * 1024 + lane * 4 + (e & 3); }
+    __device__ __forceinline__ static void owner(int off, int& lane, int& e) { lane = (off >> 2) & 255; e = (off >> 10) * 4 + (off & 3); }
     template <bool VEC>
     __device__ __forceinline__ void load(const void* row, int base, int V, int lane)
     {
@@ -275,6 +309,29 @@ struct Chunk<SV_F32> {
                 for (int h = 0; h < 4; ++h) w[4 * k + h] = (i0 + h < V) ? r[i0 + h] : -INFINITY;
             }
         }
+    }
+    template <bool VEC>
+    __device__ __forceinline__ void issue(const void* row, int base, int V, int lane)
+    {
+        if (!VEC) {
+            load<false>(row, base, V, lane);
+            return;
+        }
+        const float* r = (const float*)row;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const int i0 = base + k * 1024 + lane * 4;
+            const float4 q = *(const float4*)(r + (i0 < V ? i0 : V - 4));
+            w[4 * k] = q.x; w[4 * k + 1] = q.y; w[4 * k + 2] = q.z; w[4 * k + 3] = q.w;
+        }
+    }
+    template <bool VEC>
+    __device__ __forceinline__ void fix_tail(int base, int V, int lane)
+    {
+        if (!VEC || base + kSplit <= V) return;
+#pragma unroll
+        for (int k = 0; k < 16; ++k)
+            if (base + k * 1024 + lane * 4 >= V) w[4 * k] = w[4 * k + 1] = w[4 * k + 2] = w[4 * k + 3] = -INFINITY;
     }
 };
 
@@ -325,42 +382,77 @@ __device__ __forceinline__ double exp2_f64(double a)
 }
 
 // (max, sum exp) of one loaded split: sum in fp32 over runs of 8 elements, fp64 beyond.
+// The exponent of each term is one fma, l*c - mc with mc = m*c rounded; the
+// rounding error d = m*c - mc is exact in fp32, every term carries the factor
+// 2^d (|d| <= 2^-5), and d is returned beside the sum for the consumers to take
+// out in fp64.  The only bias left is that of c rounded to fp32 (relative
+// 2^-24 of the exponent).  Rows with |m*c| >= 2^20 take the exact-difference
+// form (d = 0).
+//
+// bf16: the sum pass widens the packed words again with byte permutes rather
+// than reusing the max pass's shifts, so the 64 widened values are never live
+// at once (registers are what bound the loads in flight).
+__device__ __forceinline__ float bf16_lo_perm(uint32_t w) { return __uint_as_float(__builtin_amdgcn_perm(w, 0u, 0x05040c0cu)); }
+__device__ __forceinline__ float bf16_hi_perm(uint32_t w) { return __uint_as_float(__builtin_amdgcn_perm(w, 0u, 0x07060c0cu)); }
+
 template <int DT>
-__device__ __forceinline__ void chunk_stats(const Chunk<DT>& c, float c_hi, float c_lo, float& M, double& S,
-                                            float* redf, double* redd)
+__device__ __forceinline__ float chunk_elem_sum(const Chunk<DT>& c, int e)
+{
+    if (DT == SV_BF16) return (e & 1) ? bf16_hi_perm(((const uint32_t*)&c)[e >> 1]) : bf16_lo_perm(((const uint32_t*)&c)[e >> 1]);
+    return c.get(e);
+}
+
+template <int DT>
+__device__ __forceinline__ void chunk_stats(const Chunk<DT>& c, float c32, float c_hi, float c_lo, float& M,
+                                            double& S, float& D, float* redf, double* redd, int t)
 {
     float m = -INFINITY;
 #pragma unroll
     for (int e = 0; e < kPerLane; ++e) m = fmaxf(m, c.get(e));
-    m = block_max(m, redf);
+    m = block_max(m, redf, t);
     double acc = 0.0;
+    float d = 0.0f;
     if (m != -INFINITY) {
+        const float mc = m * c32;
+        if (fabsf(mc) < 0x1p20f) {
+            d = fmaf(m, c32, -mc);
 #pragma unroll
-        for (int r = 0; r < kPerLane / 8; ++r) {
-            float run = 0.0f;
+            for (int r = 0; r < kPerLane / 8; ++r) {
+                float run = 0.0f;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) run += scaled_exp2(c.get(8 * r + i), m, c_hi, c_lo);
-            acc += (double)run;
+                for (int i = 0; i < 8; ++i) run += __builtin_amdgcn_exp2f(fmaf(chunk_elem_sum<DT>(c, 8 * r + i), c32, -mc));
+                acc += (double)run;
+                __builtin_amdgcn_sched_barrier(0); // widen one run at a time
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < kPerLane / 8; ++r) {
+                float run = 0.0f;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) run += scaled_exp2(chunk_elem_sum<DT>(c, 8 * r + i), m, c_hi, c_lo);
+                acc += (double)run;
+            }
         }
     }
-    S = block_sum(acc, redd);
+    S = block_sum(acc, redd, t);
+    D = d;
     M = m;
 }
 
 // (max, lowest index of the max) of one loaded split of the raw row.
 template <int DT>
 __device__ __forceinline__ void chunk_argmax(const Chunk<DT>& c, int V, int split, float& M, int& I, float* redf,
-                                             int* redi)
+                                             int* redi, int t)
 {
     float best = -INFINITY;
     int bi = 0x7fffffff;
 #pragma unroll
     for (int e = 0; e < kPerLane; ++e) {
         const float v = c.get(e);
-        const int idx = Chunk<DT>::index(split * kSplit, threadIdx.x, e);
+        const int idx = Chunk<DT>::index(split * kSplit, t, e);
         if (idx < V && (v > best || bi == 0x7fffffff)) { best = v; bi = idx; }
     }
-    block_argmax(best, bi, redf, redi);
+    block_argmax(best, bi, redf, redi, t);
     M = best;
     I = bi;
 }
@@ -415,6 +507,7 @@ __global__ __launch_bounds__(kThreads) void sv_plan_kernel(Params p, Work w)
         st.flags = FL_ACC | (len_open ? FL_LEN : 0);
     }
     w.st[b] = st;
+    w.live[b] = st.flags ? (((st.L + 1) << 2) | st.flags) : 0;
 }
 
 // ---------------------------------------------------------------- sv_rows
@@ -435,58 +528,100 @@ __device__ __forceinline__ bool draft_row_needed(int flags, int L, int j, int K)
     return j <= K && ((flags & FL_LEN) || ((flags & FL_ACC) && j <= L));
 }
 
-template <int DT, bool VEC, bool GREEDY, int SPW>
-__global__ __launch_bounds__(kThreads) void sv_rows_kernel(Params p, Work w, int j0, int G)
+// One split of one needed row: (max, sum exp2) or (max, argmax) partials, and
+// the drafted token's logit when the split holds it.
+struct RowRef {
+    const void* row;
+    int b, j, prow, split;
+};
+
+template <int DT>
+__device__ __forceinline__ RowRef row_ref(const Params& p, int b, int j, bool draft, int split)
+{
+    RowRef r;
+    r.row = draft ? row_ptr<DT>(p.d, p.dbs, p.drs, b, j - 1) : row_ptr<DT>(p.t, p.tbs, p.trs, b, j - 1);
+    r.b = b;
+    r.j = j;
+    r.prow = draft ? p.K + j : j - 1;
+    r.split = split;
+    return r;
+}
+
+// t: thread index inside the workgroup.
+template <int DT, bool GREEDY>
+__device__ __forceinline__ void rows_finish(const Params& p, const Work& w, const Chunk<DT>& c, const RowRef& r,
+                                            float* redf, double* redd, int* redi, int t)
+{
+    const long long pi = part_index(p, r.b, r.prow) + r.split;
+    if (GREEDY) {
+        float M;
+        int I;
+        chunk_argmax<DT>(c, p.V, r.split, M, I, redf, redi, t);
+        if (t == 0) {
+            w.part_m[pi] = M;
+            w.part_i[pi] = I;
+        }
+    } else {
+        // the drafted token of this position and its logit in this row, when
+        // the split holds it: r.b, r.j and x are uniform, so both come through
+        // scalar loads (the token ids and logits are never written here)
+        if (r.j <= p.K) {
+            typedef const __attribute__((address_space(4))) uint32_t* cptr;
+            const int x = (int)((cptr)p.tok)[(long long)r.b * p.K + (r.j - 1)];
+            const int off = x - r.split * kSplit;
+            if (x >= 0 && x < p.V && off >= 0 && off < kSplit) {
+                float xl;
+                if (DT == SV_BF16) {
+                    // the aligned word holding element x lies in the same page
+                    const uintptr_t a = (uintptr_t)r.row + 2 * (uintptr_t)x;
+                    const uint32_t word = *(cptr)(a & ~(uintptr_t)3);
+                    xl = (a & 2) ? bf16_hi(word) : bf16_lo(word);
+                } else {
+                    xl = __uint_as_float(((cptr)r.row)[x]);
+                }
+                if (t == 0) w.xlog[(long long)r.b * (2 * p.K + 1) + r.prow] = xl;
+            }
+        }
+        float M, D;
+        double S;
+        chunk_stats<DT>(c, p.c32, p.c_hi, p.c_lo, M, S, D, redf, redd, t);
+        if (t == 0) {
+            w.part_m[pi] = M;
+            w.part_s[pi] = S;
+            w.part_d[pi] = D;
+        }
+    }
+}
+
+// One workgroup per (sequence, row slot, split), split fastest, so that
+// consecutive workgroups stream consecutive 32 KB pieces of a row (HBM keeps
+// its rate on long contiguous runs).  A workgroup of a row the walk does not
+// need exits after one scalar load.
+template <int DT, bool VEC, bool GREEDY>
+__global__ __launch_bounds__(kThreads, (DT == SV_BF16 && VEC) ? 8 : 1) void sv_rows_kernel(Params p, Work w, int j0,
+                                                                                           int G)
 {
     __shared__ float redf[kWaves];
     __shared__ double redd[kWaves];
     __shared__ int redi[kWaves];
-    const int nchunk = (p.nsplit + SPW - 1) / SPW;
-    const int chunk = (int)(blockIdx.x % nchunk);
-    const int rest = (int)(blockIdx.x / nchunk);
+    const int t = (int)threadIdx.x;
+    const int split = (int)(blockIdx.x % (unsigned)p.nsplit);
+    const int rest = (int)(blockIdx.x / (unsigned)p.nsplit);
     const int slots = GREEDY ? G : 2 * G;
     const int slot = rest % slots;
     const int b = rest / slots;
     const bool draft = !GREEDY && slot >= G;
-    const int j = j0 + (draft ? slot - G : slot); // 1-based position
-    const int flags = w.st[b].flags;
-    const int L = w.st[b].L;
+    const int j = j0 + (draft ? slot - G : slot);
+    typedef const __attribute__((address_space(4))) int* cptr;
+    const int lv = ((cptr)w.live)[b];
+    const int flags = lv & 3, L = (lv >> 2) - 1;
     const bool need = draft ? draft_row_needed(flags, L, j, p.K) : target_row_needed(flags, L, j, p.K);
     if (!need) return;
-    const void* row = draft ? row_ptr<DT>(p.d, p.dbs, p.drs, b, j - 1) : row_ptr<DT>(p.t, p.tbs, p.trs, b, j - 1);
-    const int prow = draft ? p.K + j : j - 1;
-    const long long pbase = part_index(p, b, prow);
-    const int s0 = chunk * SPW;
-    // drafted token of this position: the workgroup whose splits hold it keeps its logit
-    const int x = (!GREEDY && threadIdx.x == 0 && j <= p.K) ? p.tok[(long long)b * p.K + (j - 1)] : -1;
-    Chunk<DT> c[2];
-    c[0].template load<VEC>(row, s0 * kSplit, p.V, threadIdx.x);
-#pragma unroll
-    for (int i = 0; i < SPW; ++i) {
-        const int split = s0 + i;
-        if (split >= p.nsplit) break;
-        if (i + 1 < SPW && split + 1 < p.nsplit) // prefetch the next split before reducing this one
-            c[(i + 1) & 1].template load<VEC>(row, (split + 1) * kSplit, p.V, threadIdx.x);
-        if (GREEDY) {
-            float M;
-            int I;
-            chunk_argmax<DT>(c[i & 1], p.V, split, M, I, redf, redi);
-            if (threadIdx.x == 0) {
-                w.part_m[pbase + split] = M;
-                w.part_i[pbase + split] = I;
-            }
-        } else {
-            float M;
-            double S;
-            chunk_stats<DT>(c[i & 1], p.c_hi, p.c_lo, M, S, redf, redd);
-            if (threadIdx.x == 0) {
-                w.part_m[pbase + split] = M;
-                w.part_s[pbase + split] = S;
-                if (x >= split * kSplit && x < (split + 1) * kSplit && x < p.V)
-                    w.xlog[(long long)b * (2 * p.K + 1) + prow] = load_one<DT>(row, x);
-            }
-        }
-    }
+    const RowRef r = row_ref<DT>(p, b, j, draft, split);
+    Chunk<DT> c;
+    c.template issue<VEC>(r.row, split * kSplit, p.V, t);
+    c.template fix_tail<VEC>(split * kSplit, p.V, t);
+    rows_finish<DT, GREEDY>(p, w, c, r, redf, redd, redi, t);
 }
 
 // ---------------------------------------------------------------- sv_decide
@@ -548,8 +683,9 @@ __global__ __launch_bounds__(kThreads) void sv_decide_kernel(Params p, Work w, i
         } else {
             const float m = has ? w.part_m[pi] : -INFINITY;
             const double sv = has ? w.part_s[pi] : 0.0;
+            const float dv = has ? w.part_d[pi] : 0.0f;
             const float M = seg_max(m, sw);
-            double v = (has && m != -INFINITY) ? sv * exp2_f64(((double)m - (double)M) * p.c64) : 0.0;
+            double v = (has && m != -INFINITY) ? sv * exp2_f64(((double)m - (double)M) * p.c64 - (double)dv) : 0.0;
             v = seg_sum(v, sw);
             if (read && k == 0) {
                 if (kind) { sMd[q] = M; sSd[q] = v; }
@@ -663,6 +799,7 @@ __global__ __launch_bounds__(kThreads) void sv_decide_kernel(Params p, Work w, i
     }
     st.flags = (acc ? FL_ACC : 0) | (len ? FL_LEN : 0);
     w.st[b] = st;
+    w.live[b] = st.flags ? (((st.L + 1) << 2) | st.flags) : 0;
 }
 
 // ---------------------------------------------------------------- final draw
@@ -862,7 +999,8 @@ __global__ __launch_bounds__(kThreads) void sv_draw_kernel(Params p, Work w)
                 if (lane < p.nsplit) {
                     const long long pb = part_index(p, b, st.js - 1) + lane;
                     const float mk = w.part_m[pb];
-                    if (mk != -INFINITY) m = w.part_s[pb] * exp2_f64(((double)mk - (double)st.Mt) * p.c64) / st.St;
+                    if (mk != -INFINITY)
+                        m = w.part_s[pb] * exp2_f64(((double)mk - (double)st.Mt) * p.c64 - (double)w.part_d[pb]) / st.St;
                 }
             }
             const double uf = (double)p.u[(long long)b * (K + 1) + K];
@@ -979,6 +1117,12 @@ __global__ __launch_bounds__(kThreads) void sv_draw_kernel(Params p, Work w)
 
 // ---------------------------------------------------------------- host side
 
+template <int DT, bool VEC, bool GR>
+void launch_rows(unsigned grid, hipStream_t s, const Params& p, const Work& w, int j0, int G)
+{
+    hipLaunchKernelGGL((sv_rows_kernel<DT, VEC, GR>), dim3(grid), dim3(kThreads), 0, s, p, w, j0, G);
+}
+
 const char* const kKernelNames[K_COUNT] = {"sv_plan", "sv_rows", "sv_decide", "sv_resid", "sv_draw"};
 constexpr int kMaxSlots = 64; // timed launches per run
 
@@ -987,7 +1131,6 @@ constexpr int kMaxSlots = 64; // timed launches per run
 struct spec_verify {
     spec_verify_config cfg;
     int nsplit;
-    int spw_sched[4];     // splits per sv_rows workgroup for groups 0, 1, 2, >= 3
     void* ws;
     Work w;
     int timing_max, timing_n;
@@ -1103,12 +1246,6 @@ int spec_verify_create(const spec_verify_config* cfg, spec_verify_t** out)
     if (!h) return SV_ENOMEM;
     h->cfg = *cfg;
     h->nsplit = nsplit_of(cfg->vocab);
-    {
-        const int def[4] = {1, 1, 2, 4};
-        for (int i = 0; i < 4; ++i) h->spw_sched[i] = def[i];
-        if (const char* e = getenv("SV_SPW_EXPERIMENT"))
-            sscanf(e, "%d,%d,%d,%d", &h->spw_sched[0], &h->spw_sched[1], &h->spw_sched[2], &h->spw_sched[3]);
-    }
     const long long nrow = (long long)cfg->max_batch * (2 * cfg->max_draft + 1);
     const size_t ns = (size_t)h->nsplit;
     size_t off = 0;
@@ -1116,7 +1253,9 @@ int spec_verify_create(const spec_verify_config* cfg, spec_verify_t** out)
     const size_t o_pm = off; off = align_up(off + nrow * ns * sizeof(float));
     const size_t o_ps = off; off = align_up(off + nrow * ns * sizeof(double));
     const size_t o_pi = off; off = align_up(off + nrow * ns * sizeof(int));
+    const size_t o_pd = off; off = align_up(off + nrow * ns * sizeof(float));
     const size_t o_st = off; off = align_up(off + (size_t)cfg->max_batch * sizeof(SeqState));
+    const size_t o_lv = off; off = align_up(off + (size_t)cfg->max_batch * sizeof(int));
     const size_t o_rs = off; off = align_up(off + (size_t)cfg->max_batch * ns * sizeof(double));
     const size_t o_sg = off; off = align_up(off + (size_t)cfg->max_batch * ns * kSegStride * sizeof(double));
     const size_t o_xl = off; off = align_up(off + nrow * sizeof(float));
@@ -1125,8 +1264,10 @@ int spec_verify_create(const spec_verify_config* cfg, spec_verify_t** out)
     h->w.ctl = (int*)(base + o_ctl);
     h->w.part_m = (float*)(base + o_pm);
     h->w.part_s = (double*)(base + o_ps);
+    h->w.part_d = (float*)(base + o_pd);
     h->w.part_i = (int*)(base + o_pi);
     h->w.st = (SeqState*)(base + o_st);
+    h->w.live = (int*)(base + o_lv);
     h->w.rsum = (double*)(base + o_rs);
     h->w.seg = (double*)(base + o_sg);
     h->w.xlog = (float*)(base + o_xl);
@@ -1247,6 +1388,7 @@ int spec_verify_run(spec_verify_t* h, const spec_verify_args* a, void* hip_strea
         if (!(lo > 1e-37f)) lo = 1e-37f;
         p.c_hi = hi;
         p.c_lo = lo;
+        p.c32 = (float)p.c64;
     }
     p.acc_out = a->accepted_len;
     p.out_tok = a->out_tokens;
@@ -1279,28 +1421,21 @@ int spec_verify_run(spec_verify_t* h, const spec_verify_args* a, void* hip_strea
 
     // groups of positions along the block: 2, 2, 4, 8, ... (a remainder of one
     // position joins the previous group)
-    int j0 = 1, gsz = 2, gidx = 0;
+    int j0 = 1, gsz = 2;
     const int npos = p.K + 1;
     while (j0 <= npos) {
         int G = gsz;
         if (npos - (j0 + G - 1) <= 1) G = npos - j0 + 1;
         if (G > kMaxGroup) G = kMaxGroup;
-        int spw = gidx < 4 ? h->spw_sched[gidx] : h->spw_sched[3];
-        if (spw > p.nsplit) spw = p.nsplit >= 4 ? 4 : (p.nsplit >= 2 ? 2 : 1);
-        const unsigned nchunk = (unsigned)((p.nsplit + spw - 1) / spw);
-        const unsigned grid = B * (unsigned)(greedy ? G : 2 * G) * nchunk;
+        const unsigned grid = (unsigned)((long long)B * (greedy ? G : 2 * G) * p.nsplit);
         mark(K_ROWS, 0);
-#define SV_ROWS(DT, VEC, GR, W) hipLaunchKernelGGL((sv_rows_kernel<DT, VEC, GR, W>), dim3(grid), dim3(kThreads), 0, s, p, h->w, j0, G)
-#define SV_ROWS_SPW(DT, VEC, GR) do { if (spw >= 4) SV_ROWS(DT, VEC, GR, 4); else if (spw == 2) SV_ROWS(DT, VEC, GR, 2); else SV_ROWS(DT, VEC, GR, 1); } while (0)
         if (bf) {
-            if (vec) { if (greedy) SV_ROWS_SPW(SV_BF16, true, true); else SV_ROWS_SPW(SV_BF16, true, false); }
-            else { if (greedy) SV_ROWS_SPW(SV_BF16, false, true); else SV_ROWS_SPW(SV_BF16, false, false); }
+            if (vec) { if (greedy) launch_rows<SV_BF16, true, true>(grid, s, p, h->w, j0, G); else launch_rows<SV_BF16, true, false>(grid, s, p, h->w, j0, G); }
+            else { if (greedy) launch_rows<SV_BF16, false, true>(grid, s, p, h->w, j0, G); else launch_rows<SV_BF16, false, false>(grid, s, p, h->w, j0, G); }
         } else {
-            if (vec) { if (greedy) SV_ROWS_SPW(SV_F32, true, true); else SV_ROWS_SPW(SV_F32, true, false); }
-            else { if (greedy) SV_ROWS_SPW(SV_F32, false, true); else SV_ROWS_SPW(SV_F32, false, false); }
+            if (vec) { if (greedy) launch_rows<SV_F32, true, true>(grid, s, p, h->w, j0, G); else launch_rows<SV_F32, true, false>(grid, s, p, h->w, j0, G); }
+            else { if (greedy) launch_rows<SV_F32, false, true>(grid, s, p, h->w, j0, G); else launch_rows<SV_F32, false, false>(grid, s, p, h->w, j0, G); }
         }
-#undef SV_ROWS_SPW
-#undef SV_ROWS
         mark(K_ROWS, 1);
         mark(K_DECIDE, 0);
         if (bf) {
@@ -1312,7 +1447,6 @@ int spec_verify_run(spec_verify_t* h, const spec_verify_args* a, void* hip_strea
         }
         mark(K_DECIDE, 1);
         j0 += G;
-        ++gidx;
         gsz = gsz < kMaxGroup ? (j0 <= 3 ? 2 : gsz * 2) : kMaxGroup;
     }
 

@@ -182,3 +182,28 @@ def test_handle_reuse_with_smaller_batch():
     _run_case("reuse big", big, sv=sv)
     _run_case("reuse small", small, sv=sv)
     sv.close()
+
+
+def _to_bf16_bits(x):
+    """float32 -> bf16 bit patterns, round to nearest even (finite inputs)."""
+    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    return ((b + 0x7FFF + ((b >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("dtype", [synth.F32, synth.BF16])
+def test_offset_logits(dtype):
+    """Rows shifted far from zero: large split maxima (the exponent's constant
+    term m*c is then rounded far from exact), maxima beyond 2^20 / c (the
+    exact-difference path), and 1e30 (every finite logit equal in fp32, so p
+    and q are uniform)."""
+    w = BASE.with_(B=8, K=4, V=20000, dtype=synth.F32, seed=37)
+    prob = synth.make_problem(w)
+    offs = [3000.0, -3000.0, 250.0, -1.0e5, 1.0e30, -1.0e30, 3.0e6, 7.5]
+    for b, o in enumerate(offs):
+        prob.target[b] += np.float32(o)
+        prob.draft[b] += np.float32(o)
+    if dtype == synth.BF16:
+        prob.target = _to_bf16_bits(prob.target)
+        prob.draft = _to_bf16_bits(prob.draft)
+        prob.w = w.with_(dtype=synth.BF16)
+    _run_case(f"offset logits dt={dtype}", prob.w, prob=prob)
