@@ -86,7 +86,7 @@ def traffic_entry(src_hash: str):
     return t.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(prob, L_total, seconds=10.0, max_reps=8):
+def cpu_baseline(prob, L_total, seconds=10.0, max_reps=200):
     from oracle import oracle as O
     threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
     threads = max(1, min(threads, len(os.sched_getaffinity(0))))
@@ -222,7 +222,10 @@ def main():
                    "input_sets": 2},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic, "kernel": dom,
-                     "kernel_avg_ms": dom_ms, "algorithmic_bytes_per_launch": bytes_step},
+                     "kernel_avg_ms": dom_ms, "algorithmic_bytes_per_launch": bytes_step,
+                     "per_launch_means": "per step: the sv_rows launches of one step (one per position group)",
+                     "traffic_source": "rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated, bytes per step; null "
+                                       "when the kernel source changed since the counters were taken"},
         "step_hbm_gbps": bytes_step / (ms_step / 1e3) / 1e9,
         "emitted_tokens_per_s": float(np.mean([o["accepted_len"].sum() + w.B for o in outs])) / (ms_step / 1e3),
         "mean_accepted": mean_a,
