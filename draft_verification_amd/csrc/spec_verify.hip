@@ -37,13 +37,15 @@
 // sv_plan (first) sets up per-sequence state and the verify length where it
 // is known without reading logits.
 //
-// Numerics.  bf16 and fp32 inputs are exact in fp32.  Per element the kernels
-// form a = (l - m) * log2(e)/T with the constant split in two fp32 parts (so
-// the scale carries no systematic rounding bias) and take v_exp_f32 (measured
-// on MI355X: < 0.8 ulp for arguments >= -12).  Sums run in fp32 over 8
-// elements and in fp64 beyond, so a row sum carries ~1e-8 relative error.
+// Numerics.  bf16 and fp32 inputs are exact in fp32.  The row statistics take
+// one fma per element, l*c - round(m*c) with c = log2(e)/T in fp32, and keep
+// the exact rounding error of m*c beside the split sum for the fp64 merges;
+// the final draw forms a = (l - m) * log2(e)/T with the constant split in two
+// fp32 parts (no systematic scale bias).  v_exp_f32 measured on MI355X:
+// < 0.8 ulp for arguments >= -12.  Sums run in fp32 over 8 elements and in
+// fp64 beyond, so a row sum carries ~1e-8 relative error.
 // Decisions (acceptance ratio, survival product, CDF prefix) are taken in fp64.
-// The final draw evaluates large masses (> 2^-12) in fp64.
+// The final draw evaluates large masses (> 2^-9) in fp64.
 //
 // Determinism.  Split boundaries depend only on V, every reduction has a fixed
 // order and there are no floating-point atomics, so outputs are bitwise
