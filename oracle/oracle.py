@@ -55,6 +55,16 @@ class _Result(ctypes.Structure):
         "residual_mass", "sampled_prob", "final_kind", "margin", "accept_gap", "cdf_gap", "alt_token")]
 
 
+class _SchedProblem(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("K", ctypes.c_int32), ("confidence", ctypes.c_void_p),
+                ("speed", ctypes.c_void_p), ("n_speed", ctypes.c_int32)]
+
+
+class _SchedResult(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "verify_len", "survival", "admitted", "tau", "expected", "margin", "bad")]
+
+
 _lib = None
 
 
@@ -68,6 +78,8 @@ def lib():
         L.svo_verify.argtypes = [ctypes.POINTER(_Problem), ctypes.POINTER(_Result)]
         L.svo_max_threads.restype = ctypes.c_int
         L.svo_max_threads.argtypes = []
+        L.svo_schedule.restype = ctypes.c_int
+        L.svo_schedule.argtypes = [ctypes.POINTER(_SchedProblem), ctypes.POINTER(_SchedResult)]
         _lib = L
     return _lib
 
@@ -164,3 +176,39 @@ def verify_problem(prob, seqs=None, all_rows=False, threads=0) -> OracleResult:
 
 def max_threads() -> int:
     return int(lib().svo_max_threads())
+
+
+@dataclass
+class ScheduleResult:
+    verify_len: np.ndarray   # [B] int32
+    survival: np.ndarray     # [B][K] float64
+    admitted: int            # m
+    tau: float               # smallest admitted survival (NaN if none)
+    expected: float          # T(m) = (B + sum of admitted survivals) * speed[B + m]
+    margin: bool             # a stop decision at or before m was a near tie
+    bad: bool                # a confidence was outside [0, 1]
+
+
+def schedule(confidence: np.ndarray, speed: np.ndarray) -> ScheduleResult:
+    """Load-aware admission (sv_oracle.c ``svo_schedule``): rank every drafted
+    position by survival and admit while expected tokens x step rate rises.
+
+    confidence: [B][K] float32; speed: steps per second at a batch of n tokens,
+    n = 0 .. B (K + 1) at least."""
+    c = np.ascontiguousarray(confidence, dtype=np.float32)
+    B, K = c.shape
+    sp = np.ascontiguousarray(speed, dtype=np.float64)
+    vl = np.zeros(B, np.int32)
+    surv = np.zeros((B, K), np.float64)
+    adm = np.zeros(1, np.int32)
+    tau = np.zeros(1, np.float64)
+    exp_ = np.zeros(1, np.float64)
+    mar = np.zeros(1, np.int32)
+    bad = np.zeros(1, np.int32)
+    prob = _SchedProblem(B, K, c.ctypes.data, sp.ctypes.data, sp.size)
+    res = _SchedResult(vl.ctypes.data, surv.ctypes.data, adm.ctypes.data, tau.ctypes.data, exp_.ctypes.data,
+                       mar.ctypes.data, bad.ctypes.data)
+    rc = lib().svo_schedule(ctypes.byref(prob), ctypes.byref(res))
+    if rc != 0:
+        raise ValueError(f"svo_schedule failed ({rc})")
+    return ScheduleResult(vl, surv, int(adm[0]), float(tau[0]), float(exp_[0]), bool(mar[0]), bool(bad[0]))

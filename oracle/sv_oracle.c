@@ -392,3 +392,110 @@ int svo_max_threads(void)
     return 1;
 #endif
 }
+
+/* ======================================================================
+ * Load-aware admission: how many drafted positions each sequence verifies.
+ *
+ * umans.ai blog, section "2. Verify smarter: a throttle that costs the user
+ * nothing": the engine's step rate is profiled against batch size once; each
+ * step the expected system throughput is the expected number of accepted
+ * tokens times the step rate at that batch size; every candidate token of
+ * every request is ranked by its survival probability and admitted one at a
+ * time until that product stops rising.  zhichai.net article, section "Under
+ * the hood": each request's verified prefix is chosen to maximise accepted
+ * tokens times verification speed.
+ *
+ * Readings (listed in the design notes):
+ *  - a candidate is drafted position j of sequence b, with survival
+ *    S_bj = prod_{i<=j} c_bi (fp64, left to right);
+ *  - confidences outside [0, 1] (NaN included) are clamped into it (NaN -> 0)
+ *    and reported as bad input;
+ *  - the verify batch of m admitted candidates holds B + m tokens (every
+ *    sequence also scores its own next position); the expected number of
+ *    emitted tokens is B + the sum of the admitted survivals;
+ *  - ranking: S descending, then b ascending, then j ascending (with c in
+ *    [0, 1], S does not increase along a sequence, so every sequence's
+ *    admitted positions are a prefix 1..L_b);
+ *  - T(m) = (B + sum of the m best survivals) * speed[B + m]; admission stops
+ *    at the first m with T(m + 1) <= T(m) ("stops rising"), m = N if never.
+ * ====================================================================== */
+
+typedef struct {
+    int32_t B, K;
+    const float* confidence;  /* [B][K] */
+    const double* speed;      /* [n_speed] steps per second at a batch of n tokens */
+    int32_t n_speed;          /* >= B (K + 1) + 1 */
+} svo_sched_problem;
+
+typedef struct {
+    int32_t* verify_len;      /* [B] */
+    double* survival;         /* [B][K] */
+    int32_t* admitted;        /* [1] m */
+    double* tau;              /* [1] smallest admitted survival, NaN if none */
+    double* expected;         /* [1] T(m) */
+    int32_t* margin;          /* [1] 1 if a stop decision at or before m was within 1e-9 (relative) */
+    int32_t* bad;             /* [1] 1 if a confidence was outside [0, 1] */
+} svo_sched_result;
+
+typedef struct { double s; int32_t b, j; } svo_cand;
+
+static int svo_cand_cmp(const void* x, const void* y)
+{
+    const svo_cand* a = (const svo_cand*)x;
+    const svo_cand* c = (const svo_cand*)y;
+    if (a->s > c->s) return -1;
+    if (a->s < c->s) return 1;
+    if (a->b != c->b) return a->b < c->b ? -1 : 1;
+    return a->j < c->j ? -1 : (a->j > c->j);
+}
+
+int svo_schedule(const svo_sched_problem* P, const svo_sched_result* R)
+{
+    const int32_t B = P->B, K = P->K;
+    const int64_t N = (int64_t)B * K;
+    if (B < 0 || K < 1 || P->n_speed < (int64_t)B * (K + 1) + 1) return -1;
+    int bad = 0;
+    svo_cand* cand = (svo_cand*)malloc(sizeof(svo_cand) * (size_t)(N > 0 ? N : 1));
+    if (!cand) return -2;
+    /* survivals */
+    for (int32_t b = 0; b < B; ++b) {
+        double S = 1.0;
+        for (int32_t j = 0; j < K; ++j) {
+            double c = (double)P->confidence[(int64_t)b * K + j];
+            if (!(c >= 0.0 && c <= 1.0)) {
+                bad = 1;
+                c = c > 1.0 ? 1.0 : 0.0; /* NaN and negatives -> 0 */
+            }
+            S *= c;
+            R->survival[(int64_t)b * K + j] = S;
+            cand[(int64_t)b * K + j].s = S;
+            cand[(int64_t)b * K + j].b = b;
+            cand[(int64_t)b * K + j].j = j;
+        }
+    }
+    /* rank every candidate by survival */
+    qsort(cand, (size_t)N, sizeof(svo_cand), svo_cand_cmp);
+    /* admit one at a time while the expected throughput rises */
+    double P_m = 0.0;                     /* sum of the m best survivals */
+    int64_t m = 0;
+    int margin = 0;
+    for (;;) {
+        const double T_m = ((double)B + P_m) * P->speed[B + m];
+        if (m == N) break;
+        const double T_next = ((double)B + P_m + cand[m].s) * P->speed[B + m + 1];
+        const double scale = fmax(fabs(T_m), fabs(T_next));
+        if (fabs(T_next - T_m) <= 1e-9 * scale) margin = 1;
+        if (T_next <= T_m) break;         /* the product stops rising */
+        P_m += cand[m].s;
+        ++m;
+    }
+    for (int32_t b = 0; b < B; ++b) R->verify_len[b] = 0;
+    for (int64_t i = 0; i < m; ++i) R->verify_len[cand[i].b]++;
+    *R->admitted = (int32_t)m;
+    *R->tau = m > 0 ? cand[m - 1].s : NAN;
+    *R->expected = ((double)B + P_m) * P->speed[B + m];
+    *R->margin = margin;
+    *R->bad = bad;
+    free(cand);
+    return 0;
+}
