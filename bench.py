@@ -111,6 +111,31 @@ def cpu_baseline(prob, L_total, seconds=10.0, max_reps=200):
                       f"in {el:.2f} s on the host CPU ({cpu_model})"}
 
 
+def time_admission(sv, torch, B, synth, Bn, K, steps, warmup):
+    """Time the load-aware admission decision (spec_verify_schedule) on the
+    same batch shape: seeded confidences and a linear step-time curve."""
+    conf, speed = synth.admission_inputs(0, Bn, K)
+    dev = torch.device("cuda")
+    c_d = torch.from_numpy(conf).to(dev)
+    s_d = torch.from_numpy(speed).to(dev)
+    vl = torch.empty(Bn, dtype=torch.int32, device=dev)
+    adm = torch.empty(1, dtype=torch.int32, device=dev)
+    a = B.make_sched_args(Bn, K, confidence=c_d, speed=s_d, n_speed=speed.size, verify_len_out=vl, admitted=adm)
+    stream = torch.cuda.current_stream().cuda_stream
+    for _ in range(max(warmup, 3)):
+        sv.schedule(a, stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        sv.schedule(a, stream)
+    e1.record()
+    torch.cuda.synchronize()
+    return {"us_per_call": e0.elapsed_time(e1) / steps * 1e3, "B": Bn, "K": K, "candidates": Bn * K,
+            "admitted": int(adm.item()),
+            "inputs": "confidences uniform in [0.3, 1) (Philox key 500), step time 20 + 0.05 n"}
+
+
 def copy_calibration():
     import torch
     n = 1 << 30
@@ -187,6 +212,7 @@ def main():
     torch.cuda.synchronize()
     kms, nruns = sv.timing_end()
     kernel_avg_ms = {k: v / max(nruns, 1) for k, v in kms.items()}
+    admission = time_admission(sv, torch, B, synth, w.B, w.K, args.steps, args.warmup)
     sv.close()
 
     L_total = [int(o["verify_len_out"].sum()) for o in outs]
@@ -234,6 +260,7 @@ def main():
         "rows_per_step": sum(a["rows"] for a in acc) / 2.0,
         "kernel_avg_ms": kernel_avg_ms,
         "kernel_src_sha": src_hash,
+        "admission": admission,
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on the same workload ...")

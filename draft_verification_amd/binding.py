@@ -22,8 +22,9 @@ SV_STATUS_BAD_INPUT, SV_STATUS_TIMEOUT = 1, 2
 EXPORTED = (
     "spec_verify_create", "spec_verify_check", "spec_verify_run", "spec_verify_destroy",
     "spec_verify_status_string", "spec_verify_timing_begin", "spec_verify_timing_end",
-    "spec_verify_kernel_count", "spec_verify_kernel_name",
+    "spec_verify_kernel_count", "spec_verify_kernel_name", "spec_verify_sched_check", "spec_verify_schedule",
 )
+SV_MAX_SCHED_BATCH, SV_MAX_SCHED_CANDIDATES = 4096, 65536
 
 
 class Config(ctypes.Structure):
@@ -44,6 +45,15 @@ class Args(ctypes.Structure):
         ("accepted_len", ctypes.c_void_p), ("out_tokens", ctypes.c_void_p), ("verify_len_out", ctypes.c_void_p),
         ("lse_target", ctypes.c_void_p), ("lse_draft", ctypes.c_void_p), ("survival", ctypes.c_void_p),
         ("residual_mass", ctypes.c_void_p), ("sampled_prob", ctypes.c_void_p), ("rows_read", ctypes.c_void_p),
+        ("device_status", ctypes.c_void_p),
+    ]
+
+
+class SchedArgs(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int32), ("K", ctypes.c_int32), ("confidence", ctypes.c_void_p), ("speed", ctypes.c_void_p),
+        ("n_speed", ctypes.c_int32), ("verify_len_out", ctypes.c_void_p), ("survival", ctypes.c_void_p),
+        ("admitted", ctypes.c_void_p), ("tau", ctypes.c_void_p), ("expected_rate", ctypes.c_void_p),
         ("device_status", ctypes.c_void_p),
     ]
 
@@ -83,6 +93,10 @@ def lib() -> ctypes.CDLL:
         L.spec_verify_kernel_count.argtypes = []
         L.spec_verify_kernel_name.restype = ctypes.c_char_p
         L.spec_verify_kernel_name.argtypes = [ctypes.c_int32]
+        L.spec_verify_sched_check.restype = ctypes.c_int
+        L.spec_verify_sched_check.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(SchedArgs)]
+        L.spec_verify_schedule.restype = ctypes.c_int
+        L.spec_verify_schedule.argtypes = [ctypes.c_void_p, ctypes.POINTER(SchedArgs), ctypes.c_void_p]
         _lib = L
     return _lib
 
@@ -126,6 +140,18 @@ def check(cfg: Config, args: Args) -> int:
     return int(lib().spec_verify_check(ctypes.byref(cfg), ctypes.byref(args)))
 
 
+def make_sched_args(B: int, K: int, *, confidence, speed, n_speed: int, verify_len_out, survival=None,
+                    admitted=None, tau=None, expected_rate=None, device_status=None) -> SchedArgs:
+    """Fill a SchedArgs struct (device tensors or addresses)."""
+    return SchedArgs(B, K, _addr(confidence), _addr(speed), int(n_speed), _addr(verify_len_out), _addr(survival),
+                     _addr(admitted), _addr(tau), _addr(expected_rate), _addr(device_status))
+
+
+def sched_check(cfg: Config, args: SchedArgs) -> int:
+    """Host-only check of an admission call (no device work)."""
+    return int(lib().spec_verify_sched_check(ctypes.byref(cfg), ctypes.byref(args)))
+
+
 class SpecVerify:
     """Owns one spec_verify handle (and its device workspace)."""
 
@@ -145,6 +171,15 @@ class SpecVerify:
         rc = lib().spec_verify_run(self._h, ctypes.byref(args), ctypes.c_void_p(stream))
         if rc != SV_OK:
             raise SpecVerifyError(rc, "spec_verify_run")
+
+    def schedule(self, args: SchedArgs, stream: Optional[int] = None) -> None:
+        """Enqueue the load-aware admission decision on ``stream``."""
+        if stream is None:
+            import torch
+            stream = torch.cuda.current_stream(self.cfg.device).cuda_stream
+        rc = lib().spec_verify_schedule(self._h, ctypes.byref(args), ctypes.c_void_p(stream))
+        if rc != SV_OK:
+            raise SpecVerifyError(rc, "spec_verify_schedule")
 
     def timing_begin(self, max_calls: int) -> None:
         rc = lib().spec_verify_timing_begin(self._h, int(max_calls))

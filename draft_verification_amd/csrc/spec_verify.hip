@@ -69,7 +69,7 @@ constexpr int kSplit = 16384;                     // elements per split (fixed f
 constexpr int kPerLane = kSplit / kThreads;       // 64 elements per lane per split
 constexpr int kMaxGroup = 16;                     // positions per group
 
-enum { CTL_STATUS = 0, CTL_WORDS = 64 };
+enum { CTL_STATUS = 0, CTL_SCHED_STATUS = 1, CTL_WORDS = 64 };
 enum { FL_ACC = 1, FL_LEN = 2 };
 enum { KIND_NONE = -1, KIND_RESID = 0, KIND_BONUS = 1, KIND_GREEDY = 2, KIND_BAD = 3 };
 enum { K_PLAN = 0, K_ROWS = 1, K_DECIDE = 2, K_RESID = 3, K_DRAW = 4, K_COUNT = 5 };
@@ -99,6 +99,9 @@ struct Work {
     double* rsum;     // [max_batch][nsplit] residual mass per split
     double* seg;      // [max_batch][nsplit][64] residual mass per segment of a split
     float* xlog;      // [max_batch][2K+1] logit of the drafted token in each row
+    double* sched_s;  // [B][K] survivals of the admission scheduler
+    int* sched_rank;  // [B][K] rank of each drafted position by survival
+    double* sched_sorted; // [B K] survivals in rank order
 };
 
 struct Params {
@@ -464,7 +467,6 @@ __device__ __forceinline__ void chunk_argmax(const Chunk<DT>& c, int V, int spli
 __global__ __launch_bounds__(kThreads) void sv_plan_kernel(Params p, Work w)
 {
     const long long i = (long long)blockIdx.x * kThreads + threadIdx.x;
-    if (i == 0) w.ctl[CTL_STATUS] = 0;
     if (i >= p.B) return;
     const int b = (int)i, K = p.K;
     SeqState st;
@@ -1113,7 +1115,154 @@ __global__ __launch_bounds__(kThreads) void sv_draw_kernel(Params p, Work w)
         if (p.zmass) p.zmass[b] = zrep;
         if (p.pys) p.pys[b] = py;
         if (p.rows_out) p.rows_out[b] = st.rows;
-        if (b == 0 && p.status_out) *p.status_out = w.ctl[CTL_STATUS];
+        if (b == 0) {
+            // every kernel that can raise a status bit has finished; the word
+            // starts the next call at zero (it is zero from create on)
+            if (p.status_out) *p.status_out = w.ctl[CTL_STATUS];
+            w.ctl[CTL_STATUS] = 0;
+        }
+    }
+}
+
+// ---------------------------------------------------------------- admission
+//
+// Load-aware admission (umans.ai blog, "2. Verify smarter: a throttle that
+// costs the user nothing"; zhichai.net article, "Under the hood"): every
+// drafted position of every sequence is ranked by its survival S_bj =
+// prod_{i<=j} c_bi and admitted one at a time while
+//   T(m) = (B + sum of the m best survivals) * speed[B + m]
+// rises (a verify batch of m admitted positions holds B + m tokens).  Ties
+// rank by sequence, then position, so each sequence's admitted positions are
+// its first L_b.  Confidences outside [0, 1] are clamped (NaN -> 0) and raise
+// SV_STATUS_BAD_INPUT.
+
+struct SchedParams {
+    int B, K, n_speed;
+    const float* conf;
+    const double* speed;
+    int* vl_out;
+    float* surv;
+    int* admitted;
+    float* tau;
+    double* expected;
+    int* status_out;
+};
+
+// survivals, left to right in fp64, one thread per sequence
+__global__ __launch_bounds__(kThreads) void sv_sched_surv_kernel(SchedParams q, Work w)
+{
+    const int b = (int)(blockIdx.x * kThreads + threadIdx.x);
+    if (b >= q.B) return;
+    double S = 1.0;
+    bool bad = false;
+    for (int j = 0; j < q.K; ++j) {
+        const long long i = (long long)b * q.K + j;
+        double c = (double)q.conf[i];
+        if (!(c >= 0.0 && c <= 1.0)) {
+            bad = true;
+            c = c > 1.0 ? 1.0 : 0.0;
+        }
+        S *= c;
+        w.sched_s[i] = S;
+        if (q.surv) q.surv[i] = (float)S;
+    }
+    if (bad) or_status(&w.ctl[CTL_SCHED_STATUS], SV_STATUS_BAD_INPUT);
+}
+
+// Rank of each drafted position in the descending order.  Every sequence's
+// survivals are already non-increasing, so the rank of (b, j) is j plus, for
+// every other sequence b', the number of its survivals that rank before S_bj:
+// those > S_bj, and for b' < b also those equal to it (one binary search per
+// sequence).  One workgroup per position, threads over sequences.
+__global__ __launch_bounds__(kThreads) void sv_sched_rank_kernel(SchedParams q, Work w)
+{
+    __shared__ double red[kWaves];
+    const int i = blockIdx.x;
+    const int b = i / q.K, j = i % q.K;
+    const double x = w.sched_s[i];
+    double cnt = 0.0; // counts are small integers: exact in fp64
+    for (int bb = threadIdx.x; bb < q.B; bb += kThreads) {
+        if (bb == b) continue;
+        const double* s = w.sched_s + (long long)bb * q.K;
+        const bool ge = bb < b; // count equal survivals too
+        int lo = 0, hi = q.K;   // first index whose survival ranks after x
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            const bool before = ge ? s[mid] >= x : s[mid] > x;
+            if (before) lo = mid + 1;
+            else hi = mid;
+        }
+        cnt += (double)lo;
+    }
+    const long long rank = (long long)j + (long long)block_sum(cnt, red);
+    if (threadIdx.x == 0) {
+        w.sched_rank[i] = (int)rank;
+        w.sched_sorted[rank] = x;
+    }
+}
+
+// One workgroup of 1024 threads: prefix sums of the ranked survivals (each
+// thread sums a run of consecutive ranks, then the run totals are scanned in a
+// fixed order), the first m at which T stops rising, and the outputs.
+constexpr int kSchedThreads = 1024;
+
+__global__ __launch_bounds__(kSchedThreads) void sv_sched_pick_kernel(SchedParams q, Work w)
+{
+    __shared__ double s_scan[kSchedThreads];
+    __shared__ int s_first[kSchedThreads / 64];
+    __shared__ int s_m;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int N = q.B * q.K;
+    const int per = (N + kSchedThreads - 1) / kSchedThreads;
+    const int m0 = tid * per, m1 = min(N, m0 + per);
+    double run = 0.0;
+    for (int m = m0; m < m1; ++m) run += w.sched_sorted[m];
+    s_scan[tid] = run;
+    __syncthreads();
+    for (int o = 1; o < kSchedThreads; o <<= 1) { // inclusive scan, fixed order
+        const double v = tid >= o ? s_scan[tid - o] : 0.0;
+        __syncthreads();
+        s_scan[tid] += v;
+        __syncthreads();
+    }
+    const double base = (tid > 0 ? s_scan[tid - 1] : 0.0) + (double)q.B; // B + P(m0)
+    // first m in this thread's run with T(m+1) <= T(m)
+    int first = 0x7fffffff;
+    double Pm = base;
+    for (int m = m0; m < m1; ++m) {
+        const double s = w.sched_sorted[m];
+        const double Tm = Pm * q.speed[q.B + m];
+        const double Tn = (Pm + s) * q.speed[q.B + m + 1];
+        if (Tn <= Tm) { first = m; break; }
+        Pm += s;
+    }
+    for (int o = 32; o > 0; o >>= 1) first = min(first, __shfl_xor(first, o));
+    if (lane == 0) s_first[wv] = first;
+    __syncthreads();
+    if (tid == 0) {
+        int f = 0x7fffffff;
+        for (int k = 0; k < kSchedThreads / 64; ++k) f = min(f, s_first[k]);
+        s_m = f == 0x7fffffff ? N : f;
+    }
+    __syncthreads();
+    const int M = s_m;
+    // the thread whose run holds M (the last non-empty run when M = N) reports T(M)
+    const bool owner = M < N ? (M >= m0 && M < m1) : (m0 < m1 && m1 == N);
+    if (owner) {
+        double P = base;
+        for (int m = m0; m < M; ++m) P += w.sched_sorted[m];
+        if (q.expected) *q.expected = P * q.speed[q.B + M];
+        if (q.admitted) *q.admitted = M;
+        if (q.tau) *q.tau = M > 0 ? (float)w.sched_sorted[M - 1] : NAN;
+    }
+    for (int b = tid; b < q.B; b += kSchedThreads) {
+        int L = 0;
+        for (int j = 0; j < q.K; ++j) L += w.sched_rank[(long long)b * q.K + j] < M ? 1 : 0;
+        q.vl_out[b] = L;
+    }
+    if (tid == 0) {
+        if (q.status_out) *q.status_out = w.ctl[CTL_SCHED_STATUS];
+        w.ctl[CTL_SCHED_STATUS] = 0;
     }
 }
 
@@ -1261,6 +1410,10 @@ int spec_verify_create(const spec_verify_config* cfg, spec_verify_t** out)
     const size_t o_rs = off; off = align_up(off + (size_t)cfg->max_batch * ns * sizeof(double));
     const size_t o_sg = off; off = align_up(off + (size_t)cfg->max_batch * ns * kSegStride * sizeof(double));
     const size_t o_xl = off; off = align_up(off + nrow * sizeof(float));
+    const long long ncand = std::min((long long)cfg->max_batch * cfg->max_draft, (long long)SV_MAX_SCHED_CANDIDATES);
+    const size_t o_ss = off; off = align_up(off + (size_t)ncand * sizeof(double));
+    const size_t o_sr = off; off = align_up(off + (size_t)ncand * sizeof(int));
+    const size_t o_so = off; off = align_up(off + (size_t)ncand * sizeof(double));
     if (hipMalloc(&h->ws, off) != hipSuccess) { free(h); return SV_ENOMEM; }
     char* base = (char*)h->ws;
     h->w.ctl = (int*)(base + o_ctl);
@@ -1273,6 +1426,15 @@ int spec_verify_create(const spec_verify_config* cfg, spec_verify_t** out)
     h->w.rsum = (double*)(base + o_rs);
     h->w.seg = (double*)(base + o_sg);
     h->w.xlog = (float*)(base + o_xl);
+    h->w.sched_s = (double*)(base + o_ss);
+    h->w.sched_rank = (int*)(base + o_sr);
+    h->w.sched_sorted = (double*)(base + o_so);
+    // control words (status bits) start at zero; each call clears what it reports
+    if (hipMemset(h->w.ctl, 0, CTL_WORDS * sizeof(int)) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+        (void)hipFree(h->ws);
+        free(h);
+        return SV_EDEVICE;
+    }
     *out = h;
     return SV_OK;
 }
@@ -1346,6 +1508,46 @@ int spec_verify_timing_end(spec_verify_t* h, double* ms, int32_t n_kernels, int3
     h->ev_kernel = nullptr;
     h->timing_max = h->timing_n = 0;
     return rc;
+}
+
+int spec_verify_sched_check(const spec_verify_config* cfg, const spec_verify_sched_args* a)
+{
+    int rc = check_config(cfg);
+    if (rc != SV_OK) return rc;
+    if (!a) return SV_EINVAL;
+    if (a->B < 0 || a->B > cfg->max_batch || a->K < 1 || a->K > cfg->max_draft) return SV_EINVAL;
+    if (a->B > SV_MAX_SCHED_BATCH || (long long)a->B * a->K > SV_MAX_SCHED_CANDIDATES) return SV_EUNSUPPORTED;
+    if (a->B == 0) return SV_OK;
+    if (!a->confidence || !a->speed || !a->verify_len_out) return SV_EINVAL;
+    if ((long long)a->n_speed < (long long)a->B * (a->K + 1) + 1) return SV_EINVAL;
+    return SV_OK;
+}
+
+int spec_verify_schedule(spec_verify_t* h, const spec_verify_sched_args* a, void* hip_stream)
+{
+    if (!h) return SV_EINVAL;
+    int rc = spec_verify_sched_check(&h->cfg, a);
+    if (rc != SV_OK) return rc;
+    if (a->B == 0) return SV_OK;
+    DeviceGuard guard(h->cfg.device);
+    hipStream_t s = (hipStream_t)hip_stream;
+    SchedParams q;
+    q.B = a->B;
+    q.K = a->K;
+    q.n_speed = a->n_speed;
+    q.conf = a->confidence;
+    q.speed = a->speed;
+    q.vl_out = a->verify_len_out;
+    q.surv = a->survival;
+    q.admitted = a->admitted;
+    q.tau = a->tau;
+    q.expected = a->expected_rate;
+    q.status_out = a->device_status;
+    const unsigned N = (unsigned)(a->B * a->K);
+    hipLaunchKernelGGL(sv_sched_surv_kernel, dim3((a->B + kThreads - 1) / kThreads), dim3(kThreads), 0, s, q, h->w);
+    hipLaunchKernelGGL(sv_sched_rank_kernel, dim3(N), dim3(kThreads), 0, s, q, h->w);
+    hipLaunchKernelGGL(sv_sched_pick_kernel, dim3(1), dim3(kSchedThreads), 0, s, q, h->w);
+    return hipGetLastError() == hipSuccess ? SV_OK : SV_EDEVICE;
 }
 
 int spec_verify_run(spec_verify_t* h, const spec_verify_args* a, void* hip_stream)

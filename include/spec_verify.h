@@ -167,6 +167,63 @@ int spec_verify_timing_end(spec_verify_t* h, double* ms, int32_t n_kernels, int3
 int32_t spec_verify_kernel_count(void);
 const char* spec_verify_kernel_name(int32_t k);
 
+/*
+ * Load-aware admission: how many drafted positions each sequence verifies.
+ *
+ *   umans.ai blog, section "2. Verify smarter: a throttle that costs the user
+ *   nothing": the engine's step rate is profiled once against batch size;
+ *   every step, expected throughput is expected accepted tokens times the rate
+ *   at that batch size; every candidate token of every request is ranked by
+ *   survival probability and admitted one at a time until that product stops
+ *   rising.  zhichai.net article, section "Under the hood": the verified
+ *   prefix of each request maximises accepted tokens x verification speed.
+ *
+ * This library's rule (the oracle follows the same words):
+ *   S_bj = prod_{i<=j} c_bi (fp64, left to right); every drafted position
+ *   (b, j) is ranked by S descending, then b, then j ascending; admitting the
+ *   first m gives a verify batch of B + m tokens and
+ *     T(m) = (B + sum of the m best survivals) * speed[B + m];
+ *   m is the first value with T(m + 1) <= T(m) (m = B K if none);
+ *   L_b = number of admitted positions of sequence b (always positions 1..L_b).
+ * Feed L_b to spec_verify_run as verify_len_in with SV_LEN_FIXED.
+ *
+ * Layout: confidence float [B][K] (device), speed double [n_speed] (device):
+ * steps per second of a verify batch of n tokens, finite and >= 0, n_speed >=
+ * B (K + 1) + 1.  Outputs (device, caller-allocated): verify_len_out int32 [B];
+ * optional survival float [B][K], admitted int32 [1] (m), tau float [1]
+ * (smallest admitted survival, NaN if m = 0), expected_rate double [1] (T(m)),
+ * device_status int32 [1] (SV_STATUS_BAD_INPUT if a confidence was outside
+ * [0, 1]; such values are clamped into it, NaN to 0).
+ * Limits: B <= min(max_batch, SV_MAX_SCHED_BATCH), K <= max_draft,
+ * B K <= SV_MAX_SCHED_CANDIDATES.  Errors as for spec_verify_run: host checks
+ * first (SV_EINVAL / SV_EUNSUPPORTED, nothing enqueued), SV_EDEVICE on a
+ * failed launch.  Uses the handle's workspace: calls on one handle must not
+ * overlap with each other or with spec_verify_run.  Deterministic: a
+ * fixed-order prefix, no floating-point atomics.
+ */
+#define SV_MAX_SCHED_BATCH 4096
+#define SV_MAX_SCHED_CANDIDATES 65536
+
+typedef struct {
+    int32_t B, K;
+    const float* confidence;      /* [B][K] */
+    const double* speed;          /* [n_speed] */
+    int32_t n_speed;
+    int32_t* verify_len_out;      /* [B] */
+    float* survival;              /* optional [B][K] */
+    int32_t* admitted;            /* optional [1] */
+    float* tau;                   /* optional [1] */
+    double* expected_rate;        /* optional [1] */
+    int32_t* device_status;       /* optional [1] */
+} spec_verify_sched_args;
+
+/* Host-only check of a spec_verify_schedule call.  Returns SV_OK, SV_EINVAL or
+ * SV_EUNSUPPORTED. */
+int spec_verify_sched_check(const spec_verify_config* cfg, const spec_verify_sched_args* a);
+
+/* Enqueue the admission decision on hip_stream (a hipStream_t, or NULL). */
+int spec_verify_schedule(spec_verify_t* h, const spec_verify_sched_args* a, void* hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

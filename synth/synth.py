@@ -187,6 +187,18 @@ def make_problem(w: Workload) -> Problem:
     return Problem(w, target, draft, tokens, u, verify_len, tau)
 
 
+def admission_inputs(seed: int, B: int, K: int, lo: float = 0.3, a: float = 20.0, b: float = 0.05):
+    """Seeded inputs of the admission decision: per-position confidences
+    uniform in [lo, 1) from the Philox uniform stream (key 500 + seed), and a
+    step-rate curve of a verify batch of n tokens with step time a + b n
+    (n = 0 .. B (K + 1)).  A stand-in for a confidence head and a startup
+    profile of the engine."""
+    u = uniforms(500 + seed, B * K).reshape(B, K).astype(np.float64)
+    conf = (lo + (1.0 - lo) * u).astype(np.float32)
+    n = np.arange(B * (K + 1) + 1, dtype=np.float64)
+    return conf, 1.0 / (a + b * n)
+
+
 def philox4x32_10(ctr, key):
     """Philox4x32-10 of one counter block via the C library (for tests)."""
     c = np.asarray(ctr, dtype=np.uint32)

@@ -124,3 +124,41 @@ def test_product_package_never_imports_the_oracle():
                 assert "oracle" not in (node.module or ""), fn
     src = open(os.path.join(pkg, "csrc", "spec_verify.hip")).read()
     assert "sv_oracle" not in src and "svo_" not in src
+
+
+def _sched(B, Bn=3, K=4, n_speed=None):
+    cfg = B.Config(8, 8, 1000, B.SV_BF16, 0)
+    fake = 1 << 40
+    a = B.make_sched_args(Bn, K, confidence=fake, speed=fake,
+                          n_speed=Bn * (K + 1) + 1 if n_speed is None else n_speed, verify_len_out=fake)
+    return cfg, a
+
+
+def test_sched_check_accepts_valid_arguments(B):
+    cfg, a = _sched(B)
+    assert B.sched_check(cfg, a) == B.SV_OK
+    cfg, a = _sched(B, Bn=0)
+    a.confidence = None
+    assert B.sched_check(cfg, a) == B.SV_OK
+
+
+@pytest.mark.parametrize("field,value", [
+    ("B", -1), ("B", 9), ("K", 0), ("K", 9), ("confidence", None), ("speed", None), ("verify_len_out", None),
+    ("n_speed", 3 * 5),
+])
+def test_sched_check_rejects(B, field, value):
+    cfg, a = _sched(B)
+    setattr(a, field, value)
+    assert B.sched_check(cfg, a) == B.SV_EINVAL
+
+
+def test_sched_check_limits(B):
+    cfg = B.Config(B.SV_MAX_SCHED_BATCH + 1, 64, 1000, B.SV_BF16, 0)
+    fake = 1 << 40
+    a = B.make_sched_args(B.SV_MAX_SCHED_BATCH + 1, 1, confidence=fake, speed=fake, n_speed=10 ** 6,
+                          verify_len_out=fake)
+    assert B.sched_check(cfg, a) == B.SV_EUNSUPPORTED
+    a = B.make_sched_args(2048, 64, confidence=fake, speed=fake, n_speed=10 ** 6, verify_len_out=fake)
+    assert B.sched_check(cfg, a) == B.SV_EUNSUPPORTED   # 131072 candidates
+    a = B.make_sched_args(1024, 64, confidence=fake, speed=fake, n_speed=10 ** 6, verify_len_out=fake)
+    assert B.sched_check(cfg, a) == B.SV_OK

@@ -89,3 +89,13 @@ def test_draft_tokens_follow_softmax_of_draft():
     expected = q.sum(axis=0)
     counts = np.bincount(p.tokens[:, 0], minlength=6)
     assert stats.chisquare(counts, expected).pvalue > 1e-4
+
+
+def test_admission_inputs_are_seeded_and_in_range():
+    c1, s1 = synth.admission_inputs(3, 8, 5)
+    c2, s2 = synth.admission_inputs(3, 8, 5)
+    np.testing.assert_array_equal(c1, c2)
+    np.testing.assert_array_equal(s1, s2)
+    assert c1.shape == (8, 5) and c1.dtype == np.float32
+    assert (c1 >= 0.3).all() and (c1 < 1.0).all()
+    assert s1.size == 8 * 6 + 1 and (np.diff(s1) < 0).all()
