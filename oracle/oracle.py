@@ -24,6 +24,7 @@ F32, BF16 = 0, 1
 LEN_FIXED, LEN_TAU = 0, 1
 FINAL_RESIDUAL, FINAL_BONUS, FINAL_GREEDY, FINAL_BAD_INPUT = 0, 1, 2, 3
 MARGIN_ACCEPT, MARGIN_CDF, MARGIN_SURVIVAL = 1, 2, 4
+DRAFT_PROBS, DRAFT_ONEHOT = 0, 1
 MARGIN = 1e-6
 
 
@@ -45,7 +46,7 @@ class _Problem(ctypes.Structure):
         ("tokens", ctypes.c_void_p), ("uniforms", ctypes.c_void_p), ("temperature", ctypes.c_float),
         ("length_mode", ctypes.c_int32), ("verify_len_in", ctypes.c_void_p), ("confidence", ctypes.c_void_p),
         ("tau", ctypes.c_void_p), ("seq_index", ctypes.c_void_p), ("n_seq", ctypes.c_int32),
-        ("all_rows", ctypes.c_int32), ("n_threads", ctypes.c_int32),
+        ("all_rows", ctypes.c_int32), ("n_threads", ctypes.c_int32), ("draft_mode", ctypes.c_int32),
     ]
 
 
@@ -110,12 +111,15 @@ def verify(target: np.ndarray, draft: Optional[np.ndarray], tokens: np.ndarray, 
            temperature: float, *, dtype: int, length_mode: int = LEN_FIXED,
            verify_len: Optional[np.ndarray] = None, confidence: Optional[np.ndarray] = None,
            tau: Optional[np.ndarray] = None, seqs: Optional[Sequence[int]] = None,
-           all_rows: bool = False, threads: int = 0, V: Optional[int] = None) -> OracleResult:
+           all_rows: bool = False, threads: int = 0, V: Optional[int] = None,
+           draft_mode: int = DRAFT_PROBS) -> OracleResult:
     """Run the fp64 definition on host arrays.
 
     ``target`` is [B][K+1][V] (float32, or uint16 bf16 bits when dtype == BF16),
     or [K+1][V] to share one set of rows across all B sequences (B is then taken
-    from ``tokens``).  ``draft`` likewise [B][K][V] or [K][V].
+    from ``tokens``).  ``draft`` likewise [B][K][V] or [K][V].  With
+    ``draft_mode == DRAFT_ONEHOT`` the draft distribution is the point mass at
+    each drafted token and ``draft`` is not read (may be None).
     """
     tokens = np.ascontiguousarray(tokens, dtype=np.int32)
     B, K = tokens.shape
@@ -148,7 +152,7 @@ def verify(target: np.ndarray, draft: Optional[np.ndarray], tokens: np.ndarray, 
     n = len(sidx)
     P = _Problem(B, K, Vv, dtype, _ptr(target), t_bs, Vv, _ptr(draft), d_bs, Vv, _ptr(tokens), _ptr(uniforms),
                  float(temperature), length_mode, _ptr(vl), _ptr(cf), _ptr(ta), _ptr(sidx), n,
-                 int(all_rows), int(threads))
+                 int(all_rows), int(threads), int(draft_mode))
     out = OracleResult(
         seq=sidx,
         accepted_len=np.empty(n, np.int32), out_tokens=np.empty((n, K + 1), np.int32),
@@ -171,7 +175,8 @@ def verify_problem(prob, seqs=None, all_rows=False, threads=0) -> OracleResult:
     w = prob.w
     return verify(prob.target, prob.draft, prob.tokens, prob.uniforms if w.temperature > 0 else prob.uniforms,
                   w.temperature, dtype=w.dtype, length_mode=w.length_mode, verify_len=prob.verify_len,
-                  confidence=prob.confidence, tau=prob.tau, seqs=seqs, all_rows=all_rows, threads=threads)
+                  confidence=prob.confidence, tau=prob.tau, seqs=seqs, all_rows=all_rows, threads=threads,
+                  draft_mode=getattr(w, "draft_mode", DRAFT_PROBS))
 
 
 def max_threads() -> int:

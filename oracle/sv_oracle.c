@@ -60,6 +60,12 @@ enum { SVO_F32 = 0, SVO_BF16 = 1 };
 enum { SVO_LEN_FIXED = 0, SVO_LEN_TAU = 1 };
 enum { SVO_FINAL_RESIDUAL = 0, SVO_FINAL_BONUS = 1, SVO_FINAL_GREEDY = 2, SVO_FINAL_BAD_INPUT = 3 };
 enum { SVO_MARGIN_ACCEPT = 1, SVO_MARGIN_CDF = 2, SVO_MARGIN_SURVIVAL = 4 };
+/* Draft distribution.  PROBS: q_j = softmax(draft logits / T).  ONEHOT: the
+ * drafter picked its tokens greedily, so q_j is the point mass at x_j (the
+ * `draft_sample_method: greedy` option of vLLM's DSpark support in the
+ * techvisionai blog, Chapter 7); no draft logits are read, the derived
+ * confidence max_v q_j(v) is 1, and lse of the draft rows is not reported. */
+enum { SVO_DRAFT_PROBS = 0, SVO_DRAFT_ONEHOT = 1 };
 
 #define SVO_MARGIN 1e-6
 
@@ -81,6 +87,7 @@ typedef struct {
     int32_t n_seq;
     int32_t all_rows;                /* 1: report lse of every row, not only the rows the step reads */
     int32_t n_threads;               /* <= 0: library default */
+    int32_t draft_mode;              /* SVO_DRAFT_PROBS, or SVO_DRAFT_ONEHOT: q_j is the point mass at x_j */
 } svo_problem;
 
 typedef struct {                     /* indexed by i in 0..n_seq-1 */
@@ -185,6 +192,7 @@ static void verify_one(const svo_problem* P, int32_t b, int32_t i, const svo_res
     const int32_t K = P->K, V = P->V;
     const double T = (double)P->temperature;
     const int greedy = !(T > 0.0);
+    const int onehot = P->draft_mode == SVO_DRAFT_ONEHOT;
     const int64_t tb = (int64_t)b * P->target_batch_stride;
     const int64_t db = (int64_t)b * P->draft_batch_stride;
     const int32_t* x = P->tokens + (int64_t)b * K;
@@ -233,6 +241,8 @@ static void verify_one(const svo_problem* P, int32_t b, int32_t i, const svo_res
             double c;
             if (P->confidence) {
                 c = (double)P->confidence[(int64_t)b * K + (j - 1)];
+            } else if (P->draft_mode == SVO_DRAFT_ONEHOT) {
+                c = 1.0; /* max of a point mass */
             } else {
                 NEED_D(j);
                 c = 1.0 / sm_d[j - 1].s; /* max_v q_j(v) = exp(m - m) / s */
@@ -273,11 +283,11 @@ static void verify_one(const svo_problem* P, int32_t b, int32_t i, const svo_res
             const int64_t toff = tb + (int64_t)(j - 1) * P->target_row_stride;
             const int64_t doff = db + (int64_t)(j - 1) * P->draft_row_stride;
             NEED_T(j);
-            NEED_D(j);
+            if (!onehot) NEED_D(j);
             const int32_t xj = x[j - 1];
             if (xj < 0 || xj >= V) { bad = 1; break; }
             const double p = softmax_at(sm_t[j - 1], P->target, P->dtype, toff + xj, T);
-            const double q = softmax_at(sm_d[j - 1], P->draft, P->dtype, doff + xj, T);
+            const double q = onehot ? 1.0 : softmax_at(sm_d[j - 1], P->draft, P->dtype, doff + xj, T);
             const double ratio = q > 0.0 ? p / q : INFINITY;
             const double uj = (double)u[j - 1];
             const double gap = fabs(uj - ratio);
@@ -304,7 +314,8 @@ static void verify_one(const svo_problem* P, int32_t b, int32_t i, const svo_res
                 double Zr = 0.0;
                 for (int32_t v = 0; v < V; ++v) {
                     const double p = softmax_at(sm_t[js - 1], P->target, P->dtype, toff + v, T);
-                    const double q = softmax_at(sm_d[js - 1], P->draft, P->dtype, doff + v, T);
+                    const double q = onehot ? (v == x[js - 1] ? 1.0 : 0.0)
+                                            : softmax_at(sm_d[js - 1], P->draft, P->dtype, doff + v, T);
                     r[v] = p > q ? p - q : 0.0;
                     Zr += r[v];
                 }
@@ -334,7 +345,7 @@ static void verify_one(const svo_problem* P, int32_t b, int32_t i, const svo_res
 
     if (P->all_rows && !greedy) {
         for (int32_t j = 1; j <= K + 1; ++j) NEED_T(j);
-        if (P->draft)
+        if (P->draft && !onehot)
             for (int32_t j = 1; j <= K; ++j) NEED_D(j);
     }
 
@@ -361,7 +372,8 @@ int svo_verify(const svo_problem* P, const svo_result* R)
 {
     if (!P || !R || P->B < 0 || P->K < 1 || P->V < 1 || P->n_seq < 0) return -1;
     const int greedy = !(P->temperature > 0.0f);
-    if (!greedy && (!P->draft || !P->uniforms)) return -1;
+    if (P->draft_mode != SVO_DRAFT_PROBS && P->draft_mode != SVO_DRAFT_ONEHOT) return -1;
+    if (!greedy && ((!P->draft && P->draft_mode == SVO_DRAFT_PROBS) || !P->uniforms)) return -1;
     if (P->length_mode == SVO_LEN_TAU && !P->tau) return -1;
     if (P->length_mode == SVO_LEN_TAU && greedy && !P->confidence) return -1;
     if (P->temperature < 0.0f || isnan(P->temperature)) return -1;

@@ -99,6 +99,8 @@ class Workload:
     fixed_len: Optional[int] = None   # None -> K
     tau_choices: tuple = ()           # LEN_TAU: per-sequence tau drawn from these
     seed: int = 1                     # uniforms use key seed; other streams 100+, 200+, ...
+    draft_mode: int = 0               # 0 draft probabilities; 1 one-hot drafts (the draft logits
+                                      # only serve to draw the tokens and are not handed over)
 
     def with_(self, **kw) -> "Workload":
         return replace(self, **kw)
@@ -175,6 +177,8 @@ def make_problem(w: Workload) -> Problem:
                                   draft.ctypes.data if draft is not None else None, tokens.ctypes.data)
     if rc != 0:
         raise RuntimeError("planted maximum not unique; pick another seed")
+    if w.draft_mode == 1:
+        draft = None
     u = uniforms(w.seed, B * (K + 1)).reshape(B, K + 1)
     verify_len = None
     tau = None
