@@ -111,6 +111,47 @@ def cpu_baseline(prob, L_total, seconds=10.0, max_reps=200):
                       f"in {el:.2f} s on the host CPU ({cpu_model})"}
 
 
+def time_onehot(torch, B, D, synth, steps, warmup):
+    """One-hot drafts (q_j = point mass at x_j; no draft logits handed over) on
+    peaked rows where a greedy drafter is worth verifying: B=256 K=16 V=129280
+    bf16, target -1.3 ln(rank) + N(0, 0.3) at T = 0.7, drafted token = the
+    largest value of target + N(0, 0.2), every position verified."""
+    base = synth.WORKLOADS["peaked512"].with_(B=256, dtype=synth.BF16, length_mode=0, token_mode=2, draft_mode=1)
+    probs = [synth.make_problem(base.with_(seed=7 + s)) for s in (0, 1000)]
+    w = probs[0].w
+    dps = [D.from_problem(p, diagnostics=False) for p in probs]
+    sv = B.SpecVerify(w.B, w.K, w.V, w.dtype, 0)
+    stream = torch.cuda.current_stream().cuda_stream
+    argv = [dp.args() for dp in dps]
+    for i in range(warmup):
+        sv.run(argv[i % 2], stream)
+    torch.cuda.synchronize()
+    outs = [dp.fetch() for dp in dps]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        sv.run(argv[i % 2], stream)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    sv.timing_begin(steps)
+    for i in range(steps):
+        sv.run(argv[i % 2], stream)
+    torch.cuda.synchronize()
+    kms, nruns = sv.timing_end()
+    sv.close()
+    rows_ms = kms["sv_rows"] / max(nruns, 1)
+    bytes_step = sum(step_bytes(o, w)["bytes"] for o in outs) / 2.0
+    positions = sum(int(o["verify_len_out"].sum()) for o in outs) / 2.0
+    return {"value": positions / (ms / 1e3), "unit": "verified draft positions/s", "ms_per_step": ms,
+            "mean_accepted": float(np.mean([o["accepted_len"].mean() for o in outs])),
+            "sv_rows_gbps": bytes_step / (rows_ms / 1e3) / 1e9, "rows_per_step": sum(
+                int(o["rows_read"].sum()) for o in outs) / 2.0,
+            "kernel_avg_ms": {k: v / max(nruns, 1) for k, v in kms.items()},
+            "workload": "one-hot drafts (greedy drafter) on peaked rows: B=256 K=16 V=129280 bf16, "
+                        "Zipf(1.3)+N(0,0.3) at T=0.7, draft noise 0.2, L=16; target rows only"}
+
+
 def time_admission(sv, torch, B, synth, Bn, K, steps, warmup):
     """Time the load-aware admission decision (spec_verify_schedule) on the
     same batch shape: seeded confidences and a linear step-time curve."""
@@ -214,6 +255,8 @@ def main():
     kernel_avg_ms = {k: v / max(nruns, 1) for k, v in kms.items()}
     admission = time_admission(sv, torch, B, synth, w.B, w.K, args.steps, args.warmup)
     sv.close()
+    del dps, argv
+    onehot = time_onehot(torch, B, D, synth, args.steps, args.warmup)
 
     L_total = [int(o["verify_len_out"].sum()) for o in outs]
     acc = [step_bytes(o, w) for o in outs]
@@ -261,6 +304,7 @@ def main():
         "kernel_avg_ms": kernel_avg_ms,
         "kernel_src_sha": src_hash,
         "admission": admission,
+        "onehot": onehot,
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on the same workload ...")

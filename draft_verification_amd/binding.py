@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(PKG, "libspec_verify.so")
 SV_OK, SV_EINVAL, SV_ENOMEM, SV_EDEVICE, SV_EUNSUPPORTED = 0, -1, -2, -3, -4
 SV_F32, SV_BF16 = 0, 1
 SV_LEN_FIXED, SV_LEN_TAU = 0, 1
+SV_DRAFT_PROBS, SV_DRAFT_ONEHOT = 0, 1
 SV_STATUS_BAD_INPUT, SV_STATUS_TIMEOUT = 1, 2
 
 EXPORTED = (
@@ -45,7 +46,7 @@ class Args(ctypes.Structure):
         ("accepted_len", ctypes.c_void_p), ("out_tokens", ctypes.c_void_p), ("verify_len_out", ctypes.c_void_p),
         ("lse_target", ctypes.c_void_p), ("lse_draft", ctypes.c_void_p), ("survival", ctypes.c_void_p),
         ("residual_mass", ctypes.c_void_p), ("sampled_prob", ctypes.c_void_p), ("rows_read", ctypes.c_void_p),
-        ("device_status", ctypes.c_void_p),
+        ("device_status", ctypes.c_void_p), ("draft_mode", ctypes.c_int32),
     ]
 
 
@@ -123,7 +124,8 @@ def make_args(B: int, K: int, *, target, draft=None, tokens, uniforms=None, temp
               target_strides: Sequence[int], draft_strides: Sequence[int] = (0, 0),
               length_mode: int = SV_LEN_FIXED, verify_len=None, confidence=None, tau=None,
               accepted_len, out_tokens, verify_len_out, lse_target=None, lse_draft=None, survival=None,
-              residual_mass=None, sampled_prob=None, rows_read=None, device_status=None) -> Args:
+              residual_mass=None, sampled_prob=None, rows_read=None, device_status=None,
+              draft_mode: int = SV_DRAFT_PROBS) -> Args:
     """Fill an Args struct.  Strides are (batch, row) in elements."""
     return Args(
         B, K, _addr(target), int(target_strides[0]), int(target_strides[1]),
@@ -132,7 +134,7 @@ def make_args(B: int, K: int, *, target, draft=None, tokens, uniforms=None, temp
         _addr(verify_len), _addr(confidence), _addr(tau),
         _addr(accepted_len), _addr(out_tokens), _addr(verify_len_out),
         _addr(lse_target), _addr(lse_draft), _addr(survival), _addr(residual_mass), _addr(sampled_prob),
-        _addr(rows_read), _addr(device_status))
+        _addr(rows_read), _addr(device_status), int(draft_mode))
 
 
 def check(cfg: Config, args: Args) -> int:

@@ -107,6 +107,7 @@ struct Work {
 struct Params {
     int B, K, V, nsplit, seg_w;   // seg_w: the power of two >= nsplit
     int greedy, derived;       // derived: tau mode with c = max draft probability
+    int onehot;                // q_j is the point mass at x_j; no draft row is streamed
     int len_mode;
     const void* t;
     long long tbs, trs;
@@ -235,6 +236,15 @@ struct Chunk<SV_BF16> {
     __device__ __forceinline__ static int index(int base, int lane, int e) { return base + (e >> 3) * 2048 + lane * 8 + (e & 7); }
     // lane and element holding offset off (0 <= off < kSplit) of the split
     __device__ __forceinline__ static void owner(int off, int& lane, int& e) { lane = (off >> 3) & 255; e = (off >> 11) * 8 + (off & 7); }
+    // the one-hot draft row: -inf everywhere, 0 at element e of this lane (e < 0: none)
+    __device__ __forceinline__ void one_hot(int e)
+    {
+#pragma unroll
+        for (int k = 0; k < kPerLane / 2; ++k) {
+            const uint32_t lo = 2 * k == e ? 0x0000u : 0xFF80u, hi = 2 * k + 1 == e ? 0x0000u : 0xFF80u;
+            w[k] = lo | (hi << 16);
+        }
+    }
     template <bool VEC>
     __device__ __forceinline__ void load(const void* row, int base, int V, int lane)
     {
@@ -295,6 +305,11 @@ struct Chunk<SV_F32> {
     __device__ __forceinline__ float get(int e) const { return w[e]; }
     __device__ __forceinline__ static int index(int base, int lane, int e) { return base + (e >> 2) * 1024 + lane * 4 + (e & 3); }
     __device__ __forceinline__ static void owner(int off, int& lane, int& e) { lane = (off >> 2) & 255; e = (off >> 10) * 4 + (off & 3); }
+    __device__ __forceinline__ void one_hot(int e)
+    {
+#pragma unroll
+        for (int k = 0; k < kPerLane; ++k) w[k] = k == e ? 0.0f : -INFINITY;
+    }
     template <bool VEC>
     __device__ __forceinline__ void load(const void* row, int base, int V, int lane)
     {
@@ -499,8 +514,10 @@ __global__ __launch_bounds__(kThreads) void sv_plan_kernel(Params p, Work w)
         // tau > 1 (or NaN) none; otherwise the walk along the block decides.
         const float tau = p.tau[b];
         if (!(tau <= 1.0f)) L = 0;
-        else if (tau <= 0.0f) L = K;
+        else if (tau <= 0.0f || p.onehot) L = K; // one-hot drafts: c_j = 1
         else { L = -1; len_open = true; }
+        if (p.onehot && p.surv)
+            for (int j = 0; j < K; ++j) p.surv[(long long)b * K + j] = 1.0f;
     }
     st.L = L;
     if (bad) {
@@ -611,7 +628,7 @@ __global__ __launch_bounds__(kThreads, (DT == SV_BF16 && VEC) ? 8 : 1) void sv_r
     const int t = (int)threadIdx.x;
     const int split = (int)(blockIdx.x % (unsigned)p.nsplit);
     const int rest = (int)(blockIdx.x / (unsigned)p.nsplit);
-    const int slots = GREEDY ? G : 2 * G;
+    const int slots = (GREEDY || p.onehot) ? G : 2 * G; // one-hot drafts: target rows only
     const int slot = rest % slots;
     const int b = rest / slots;
     const bool draft = !GREEDY && slot >= G;
@@ -675,7 +692,7 @@ __global__ __launch_bounds__(kThreads) void sv_decide_kernel(Params p, Work w, i
         const int t = base + tid;
         const int pk = t / sw, k = t % sw;
         const int q = pk >> 1, kind = pk & 1, j = j0 + q;
-        const bool read = t < per && (kind ? (!GREEDY && draft_row_needed(flags0, L0, j, K))
+        const bool read = t < per && (kind ? (!GREEDY && !p.onehot && draft_row_needed(flags0, L0, j, K))
                                            : target_row_needed(flags0, L0, j, K));
         const bool has = read && k < p.nsplit;
         const long long pi = has ? part_index(p, b, kind ? K + j : j - 1) + k : 0;
@@ -703,9 +720,16 @@ __global__ __launch_bounds__(kThreads) void sv_decide_kernel(Params p, Work w, i
         if (kind < 2 && q < n && j <= K) {
             const bool read = kind ? draft_row_needed(flags0, L0, j, K) : target_row_needed(flags0, L0, j, K);
             if (read) {
-                const float v = w.xlog[(long long)b * (2 * K + 1) + (kind ? K + j : j - 1)];
-                if (kind) sLd[q] = v;
-                else sLt[q] = v;
+                if (kind && p.onehot) {
+                    // the one-hot draft row: logit 0 at x, -inf elsewhere (max 0, sum 1)
+                    sLd[q] = 0.0f;
+                    sMd[q] = 0.0f;
+                    sSd[q] = 1.0;
+                } else {
+                    const float v = w.xlog[(long long)b * (2 * K + 1) + (kind ? K + j : j - 1)];
+                    if (kind) sLd[q] = v;
+                    else sLt[q] = v;
+                }
             }
         }
     }
@@ -727,7 +751,7 @@ __global__ __launch_bounds__(kThreads) void sv_decide_kernel(Params p, Work w, i
                 sRatio[q] = ratio;
             }
             if (tread && p.lse_t) sLseT[q] = (float)((double)sMt[q] * p.invT64 + log(sSt[q]));
-            if (dread && p.lse_d) sLseD[q] = (float)((double)sMd[q] * p.invT64 + log(sSd[q]));
+            if (dread && p.lse_d && !p.onehot) sLseD[q] = (float)((double)sMd[q] * p.invT64 + log(sSd[q]));
         }
     }
     __syncthreads();
@@ -739,12 +763,12 @@ __global__ __launch_bounds__(kThreads) void sv_decide_kernel(Params p, Work w, i
     for (int q = 0; q < n; ++q) {
         const int j = j0 + q;
         const bool dread = !GREEDY && draft_row_needed(flags0, L0, j, K);
-        st.rows += (target_row_needed(flags0, L0, j, K) ? 1 : 0) + (dread ? 1 : 0);
+        st.rows += (target_row_needed(flags0, L0, j, K) ? 1 : 0) + ((dread && !p.onehot) ? 1 : 0);
         if (!acc && !len) continue; // rows of this group past the stop were still streamed
         if (!GREEDY) {
             if (acc && p.lse_t) p.lse_t[(long long)b * (K + 1) + (j - 1)] = sLseT[q];
-            if (dread && p.lse_d) p.lse_d[(long long)b * K + (j - 1)] = sLseD[q];
-            if (dread && p.derived) {
+            if (dread && p.lse_d && !p.onehot) p.lse_d[(long long)b * K + (j - 1)] = sLseD[q];
+            if (dread && p.derived && !p.onehot) {
                 // c_j = max_v q_j(v) = 1 / Sd; S_j = S_{j-1} c_j
                 const double S = st.S / sSd[q];
                 st.S = S;
@@ -941,7 +965,21 @@ __global__ __launch_bounds__(kThreads) void sv_resid_kernel(Params p, Work w)
     const DrawCtx c = make_ctx(st, p);
     Chunk<DT> tc, dc;
     tc.template load<VEC>(row_ptr<DT>(p.t, p.tbs, p.trs, b, st.js - 1), split * kSplit, p.V, threadIdx.x);
-    dc.template load<VEC>(row_ptr<DT>(p.d, p.dbs, p.drs, b, st.js - 1), split * kSplit, p.V, threadIdx.x);
+    if (p.onehot) {
+        // the one-hot draft row, built in registers: logit 0 at the drafted
+        // token (held by one lane of one split), -inf elsewhere
+        const int x = p.tok[(long long)b * p.K + (st.js - 1)];
+        const int off = x - split * kSplit;
+        int e = -1;
+        if (off >= 0 && off < kSplit) {
+            int ol, oe;
+            Chunk<DT>::owner(off, ol, oe);
+            if ((int)threadIdx.x == ol) e = oe;
+        }
+        dc.one_hot(e);
+    } else {
+        dc.template load<VEC>(row_ptr<DT>(p.d, p.dbs, p.drs, b, st.js - 1), split * kSplit, p.V, threadIdx.x);
+    }
     split_segments<DT>(tc, dc, c, true, s_seg);
     __syncthreads();
     const long long so = ((long long)b * p.nsplit + split) * kSegStride;
@@ -1026,7 +1064,8 @@ __global__ __launch_bounds__(kThreads) void sv_draw_kernel(Params p, Work w)
         const int ks = s_split;
         const DrawCtx c = make_ctx(st, p);
         const void* trow = row_ptr<DT>(p.t, p.tbs, p.trs, b, st.js - 1);
-        const void* drow = resid ? row_ptr<DT>(p.d, p.dbs, p.drs, b, st.js - 1) : nullptr;
+        const void* drow = (resid && !p.onehot) ? row_ptr<DT>(p.d, p.dbs, p.drs, b, st.js - 1) : nullptr;
+        const int xone = (resid && p.onehot) ? p.tok[(long long)b * K + (st.js - 1)] : -1; // one-hot draft token
 
         // 2. segment sums of that split: stored by sv_resid for a replacement,
         //    computed here for a bonus draw
@@ -1053,7 +1092,9 @@ __global__ __launch_bounds__(kThreads) void sv_draw_kernel(Params p, Work w)
 #pragma unroll
             for (int i = 0; i < S::RUN; ++i) {
                 lt[i] = i0 + i < p.V ? load_one<DT>(trow, i0 + i) : -INFINITY;
-                ld[i] = (resid && i0 + i < p.V) ? load_one<DT>(drow, i0 + i) : -INFINITY;
+                ld[i] = (resid && i0 + i < p.V)
+                            ? (p.onehot ? (i0 + i == xone ? 0.0f : -INFINITY) : load_one<DT>(drow, i0 + i))
+                            : -INFINITY;
             }
             bool slow;
             double r = run_mass<S::RUN>(lt, ld, c, resid, slow);
@@ -1089,7 +1130,8 @@ __global__ __launch_bounds__(kThreads) void sv_draw_kernel(Params p, Work w)
                 if (yy < 0) yy = lastpos >= 0 ? lastpos : i0; // rounding: last token with mass
                 s_y = yy;
                 // the reported probability of the chosen token is evaluated in fp64
-                s_my = mass_f64(load_one<DT>(trow, yy), resid ? load_one<DT>(drow, yy) : 0.0f, c, resid);
+                const float ldy = !resid ? 0.0f : (p.onehot ? (yy == xone ? 0.0f : -INFINITY) : load_one<DT>(drow, yy));
+                s_my = mass_f64(load_one<DT>(trow, yy), ldy, c, resid);
             }
         }
         __syncthreads();
@@ -1302,7 +1344,7 @@ bool args_vec_ok(const spec_verify_config* cfg, const spec_verify_args* a)
     if (cfg->vocab % per) return false;
     if ((uintptr_t)a->target_logits % 16) return false;
     if ((a->target_batch_stride * es) % 16 || (a->target_row_stride * es) % 16) return false;
-    if (a->temperature > 0.0f) {
+    if (a->temperature > 0.0f && a->draft_mode == SV_DRAFT_PROBS) {
         if ((uintptr_t)a->draft_logits % 16) return false;
         if ((a->draft_batch_stride * es) % 16 || (a->draft_row_stride * es) % 16) return false;
     }
@@ -1372,9 +1414,13 @@ int spec_verify_check(const spec_verify_config* cfg, const spec_verify_args* a)
     const int V = cfg->vocab;
     if (!a->target_logits || a->target_row_stride < V || a->target_batch_stride < 0) return SV_EINVAL;
     if (!a->draft_tokens) return SV_EINVAL;
+    if (a->draft_mode != SV_DRAFT_PROBS && a->draft_mode != SV_DRAFT_ONEHOT) return SV_EINVAL;
     if (T > 0.0f) {
-        if (!a->draft_logits || !a->uniforms) return SV_EINVAL;
-        if (a->draft_row_stride < V || a->draft_batch_stride < 0) return SV_EINVAL;
+        if (!a->uniforms) return SV_EINVAL;
+        if (a->draft_mode == SV_DRAFT_PROBS) {
+            if (!a->draft_logits) return SV_EINVAL;
+            if (a->draft_row_stride < V || a->draft_batch_stride < 0) return SV_EINVAL;
+        }
     }
     if (a->length_mode == SV_LEN_TAU) {
         if (!a->tau) return SV_EINVAL;
@@ -1572,6 +1618,7 @@ int spec_verify_run(spec_verify_t* h, const spec_verify_args* a, void* hip_strea
     p.greedy = greedy;
     p.len_mode = a->length_mode;
     p.derived = (a->length_mode == SV_LEN_TAU && !a->confidence) ? 1 : 0;
+    p.onehot = (!greedy && a->draft_mode == SV_DRAFT_ONEHOT) ? 1 : 0;
     p.t = a->target_logits;
     p.tbs = a->target_batch_stride;
     p.trs = a->target_row_stride;
@@ -1631,7 +1678,7 @@ int spec_verify_run(spec_verify_t* h, const spec_verify_args* a, void* hip_strea
         int G = gsz;
         if (npos - (j0 + G - 1) <= 1) G = npos - j0 + 1;
         if (G > kMaxGroup) G = kMaxGroup;
-        const unsigned grid = (unsigned)((long long)B * (greedy ? G : 2 * G) * p.nsplit);
+        const unsigned grid = (unsigned)((long long)B * ((greedy || p.onehot) ? G : 2 * G) * p.nsplit);
         mark(K_ROWS, 0);
         if (bf) {
             if (vec) { if (greedy) launch_rows<SV_BF16, true, true>(grid, s, p, h->w, j0, G); else launch_rows<SV_BF16, true, false>(grid, s, p, h->w, j0, G); }

@@ -52,12 +52,13 @@ class DeviceProblem:
     sampled_prob: Optional[torch.Tensor] = None
     rows_read: Optional[torch.Tensor] = None
     device_status: Optional[torch.Tensor] = None
+    draft_mode: int = B.SV_DRAFT_PROBS
 
     @staticmethod
     def upload(target: np.ndarray, draft: Optional[np.ndarray], tokens: np.ndarray,
                uniforms: Optional[np.ndarray], temperature: float, dtype: int, *,
                length_mode: int = B.SV_LEN_FIXED, verify_len=None, confidence=None, tau=None,
-               diagnostics: bool = True, device="cuda:0") -> "DeviceProblem":
+               diagnostics: bool = True, device="cuda:0", draft_mode: int = B.SV_DRAFT_PROBS) -> "DeviceProblem":
         """Copy host arrays to the GPU.  ``target`` is [B][K+1][V] or [K+1][V]
         (shared by all sequences); bf16 is passed as uint16 bit patterns."""
         Bn, K = tokens.shape
@@ -71,6 +72,7 @@ class DeviceProblem:
                            _dev(target, device), _dev(draft, device), _dev(tokens.astype(np.int32), device),
                            _dev(uniforms, device), _dev(verify_len, device), _dev(confidence, device),
                            _dev(tau, device), tstr, dstr)
+        dp.draft_mode = int(draft_mode)
         dp.alloc_outputs(diagnostics, device)
         return dp
 
@@ -99,7 +101,7 @@ class DeviceProblem:
             accepted_len=self.accepted_len, out_tokens=self.out_tokens, verify_len_out=self.verify_len_out,
             lse_target=self.lse_target, lse_draft=self.lse_draft, survival=self.survival,
             residual_mass=self.residual_mass, sampled_prob=self.sampled_prob, rows_read=self.rows_read,
-            device_status=self.device_status)
+            device_status=self.device_status, draft_mode=self.draft_mode)
 
     def fetch(self) -> dict:
         torch.cuda.synchronize()
@@ -117,7 +119,8 @@ def from_problem(prob, diagnostics: bool = True, device="cuda:0") -> DeviceProbl
     return DeviceProblem.upload(prob.target, prob.draft, prob.tokens,
                                 prob.uniforms if w.temperature > 0 else None, w.temperature, w.dtype,
                                 length_mode=w.length_mode, verify_len=prob.verify_len,
-                                confidence=prob.confidence, tau=prob.tau, diagnostics=diagnostics, device=device)
+                                confidence=prob.confidence, tau=prob.tau, diagnostics=diagnostics, device=device,
+                                draft_mode=getattr(w, "draft_mode", B.SV_DRAFT_PROBS))
 
 
 def handle_for(dp: DeviceProblem, device: int = 0, max_batch: Optional[int] = None,

@@ -22,6 +22,8 @@
  *     p of the next row by inverse CDF.
  *   T == 0 selects greedy verification: the target token is the argmax of the
  *   raw target row (lowest id on ties); x_j is accepted iff it equals it.
+ *   With draft_mode SV_DRAFT_ONEHOT, q_j is the point mass at x_j (see the
+ *   field's comment below).
  *
  *   Verify length (confidence scheduling): each draft position carries a
  *   confidence c_j, the probability that it survives given that all earlier
@@ -97,6 +99,7 @@ typedef struct spec_verify spec_verify_t; /* opaque handle */
 enum { SV_OK = 0, SV_EINVAL = -1, SV_ENOMEM = -2, SV_EDEVICE = -3, SV_EUNSUPPORTED = -4 };
 enum { SV_F32 = 0, SV_BF16 = 1 };
 enum { SV_LEN_FIXED = 0, SV_LEN_TAU = 1 };
+enum { SV_DRAFT_PROBS = 0, SV_DRAFT_ONEHOT = 1 };
 enum { SV_STATUS_BAD_INPUT = 1, SV_STATUS_TIMEOUT = 2 };
 
 /* Limits checked by spec_verify_create. */
@@ -135,6 +138,13 @@ typedef struct {
     float* sampled_prob;           /* optional [B] */
     int32_t* rows_read;            /* optional [B] */
     int32_t* device_status;        /* optional [1] */
+    int32_t draft_mode;            /* SV_DRAFT_PROBS (0): q = softmax(draft_logits / T).
+                                      SV_DRAFT_ONEHOT: the drafter chose greedily, so q_j is the
+                                      point mass at x_j (techvisionai blog, Chapter 7: vLLM's
+                                      draft_sample_method greedy).  Acceptance has probability
+                                      p_j(x_j); the replacement is p_j without x_j, renormalised;
+                                      derived c_j = 1.  draft_logits is not read (may be NULL);
+                                      lse_draft is not written; no draft row is streamed. */
 } spec_verify_args;
 
 /* Allocate a handle and its workspace on cfg->device.  *out is set only on SV_OK. */

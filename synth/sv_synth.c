@@ -145,7 +145,8 @@ typedef struct {
     double plant_value;
     int32_t make_draft;      /* 1: draft row j = target row j (fp64) + sigma_j * N(0,1) */
     double sigma_first, sigma_last; /* sigma_j linear in j from first to last position */
-    int32_t token_mode;      /* 0: x_j ~ softmax(d_j / T) (Gumbel-max); 1: planted max w.p. p_match else uniform id */
+    int32_t token_mode;      /* 0: x_j ~ softmax(d_j / T) (Gumbel-max); 1: planted max w.p. p_match else uniform id;
+                                2: the draft row's largest value (a greedy drafter) */
     double temperature, p_match;
     uint32_t seed_target, seed_draft, seed_tokens, seed_aux;
 } synth_spec;
@@ -242,6 +243,13 @@ int synth_make_problem(const synth_spec* s, void* target, void* draft, int32_t* 
             }
             if (s->token_mode == 0) {
                 tokens[drow_id] = gumbel_max_token(s, drow_id, stored);
+            } else if (s->token_mode == 2) {
+                /* a drafter that picks greedily: the first id holding the
+                 * largest stored draft value */
+                int32_t best = 0;
+                for (int32_t v = 1; v < V; ++v)
+                    if (stored[v] > stored[best]) best = v;
+                tokens[drow_id] = best;
             } else {
                 uint32_t w[4];
                 philox_block(0u, drow_id, STREAM_COIN, s->seed_tokens, w);

@@ -92,7 +92,7 @@ class Workload:
     make_draft: bool = True
     sigma_first: float = 0.5
     sigma_last: float = 0.5
-    token_mode: int = 0        # 0 sample from q, 1 planted argmax w.p. p_match
+    token_mode: int = 0        # 0 sample from q, 1 planted argmax w.p. p_match, 2 greedy drafter
     p_match: float = 0.8
     temperature: float = 1.0   # passed to the verifier; 0 = greedy
     length_mode: int = LEN_FIXED

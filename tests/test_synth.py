@@ -99,3 +99,10 @@ def test_admission_inputs_are_seeded_and_in_range():
     assert c1.shape == (8, 5) and c1.dtype == np.float32
     assert (c1 >= 0.3).all() and (c1 < 1.0).all()
     assert s1.size == 8 * 6 + 1 and (np.diff(s1) < 0).all()
+
+
+def test_greedy_drafter_tokens_are_the_draft_rows_first_maximum():
+    w = synth.WORKLOADS["tiny"].with_(B=6, K=3, V=700, dtype=synth.BF16, token_mode=2, seed=71)
+    prob = synth.make_problem(w)
+    d = synth.bf16_bits_to_f32(prob.draft)
+    np.testing.assert_array_equal(prob.tokens, np.argmax(d, axis=2))
