@@ -152,6 +152,60 @@ def time_onehot(torch, B, D, synth, steps, warmup):
                         "Zipf(1.3)+N(0,0.3) at T=0.7, draft noise 0.2, L=16; target rows only"}
 
 
+def _time_runs(torch, sv, argv, steps, warmup):
+    stream = torch.cuda.current_stream().cuda_stream
+    for i in range(warmup):
+        sv.run(argv[i % len(argv)], stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        sv.run(argv[i % len(argv)], stream)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def time_packed(torch, B, D, synth, steps, warmup):
+    """Admission then verification, as an engine would chain them: the GPU
+    scheduler picks L_b from seeded confidences (same shape as the main
+    workload), the target and draft logits then hold only the admitted rows
+    (packed, with row offsets), and the verify step runs on them.  The dense
+    layout at the same L_b is timed beside it."""
+    base = workload().with_(length_mode=0, tau_choices=())
+    Bn, K = base.B, base.K
+    conf, speed = synth.admission_inputs(0, Bn, K)
+    sv = B.SpecVerify(Bn, K, base.V, base.dtype, 0)
+    dev = torch.device("cuda")
+    vl = torch.empty(Bn, dtype=torch.int32, device=dev)
+    sv.schedule(B.make_sched_args(Bn, K, confidence=torch.from_numpy(conf).to(dev),
+                                  speed=torch.from_numpy(speed).to(dev), n_speed=speed.size, verify_len_out=vl))
+    L = vl.cpu().numpy()
+    out = {"admitted": int(L.sum()), "mean_L": float(L.mean())}
+    for layout in ("packed", "dense"):
+        dps = []
+        for s in (0, 1000):
+            prob = synth.make_problem(base.with_(seed=3 + s))
+            prob.verify_len = L.astype(np.int32)
+            dps.append(D.packed_from_problem(prob, L, diagnostics=False) if layout == "packed"
+                       else D.from_problem(prob, diagnostics=False))
+            del prob
+        ms = _time_runs(torch, sv, [d.args() for d in dps], steps, warmup)
+        outs = [d.fetch() for d in dps]
+        out[layout] = {"ms_per_step": ms, "value": float(L.sum()) / (ms / 1e3),
+                       "rows_per_step": sum(int(o["rows_read"].sum()) for o in outs) / 2.0,
+                       "logit_bytes_held": sum(int(d.target.numel() * d.target.element_size()) + (
+                           int(d.draft.numel() * d.draft.element_size()) if d.draft is not None else 0)
+                           for d in dps) / 2.0}
+        del dps, outs
+        torch.cuda.empty_cache()
+    sv.close()
+    out["unit"] = "verified draft positions/s"
+    out["workload"] = ("B=256 K=16 V=129280 bf16 rows as the main workload; L_b chosen by spec_verify_schedule "
+                       "from seeded confidences and step time 20 + 0.05 n")
+    return out
+
+
 def time_admission(sv, torch, B, synth, Bn, K, steps, warmup):
     """Time the load-aware admission decision (spec_verify_schedule) on the
     same batch shape: seeded confidences and a linear step-time curve."""
@@ -257,6 +311,7 @@ def main():
     sv.close()
     del dps, argv
     onehot = time_onehot(torch, B, D, synth, args.steps, args.warmup)
+    packed = time_packed(torch, B, D, synth, args.steps, args.warmup)
 
     L_total = [int(o["verify_len_out"].sum()) for o in outs]
     acc = [step_bytes(o, w) for o in outs]
@@ -305,6 +360,7 @@ def main():
         "kernel_src_sha": src_hash,
         "admission": admission,
         "onehot": onehot,
+        "packed": packed,
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on the same workload ...")

@@ -47,6 +47,7 @@ class Args(ctypes.Structure):
         ("lse_target", ctypes.c_void_p), ("lse_draft", ctypes.c_void_p), ("survival", ctypes.c_void_p),
         ("residual_mass", ctypes.c_void_p), ("sampled_prob", ctypes.c_void_p), ("rows_read", ctypes.c_void_p),
         ("device_status", ctypes.c_void_p), ("draft_mode", ctypes.c_int32),
+        ("target_row_offsets", ctypes.c_void_p), ("draft_row_offsets", ctypes.c_void_p),
     ]
 
 
@@ -125,7 +126,7 @@ def make_args(B: int, K: int, *, target, draft=None, tokens, uniforms=None, temp
               length_mode: int = SV_LEN_FIXED, verify_len=None, confidence=None, tau=None,
               accepted_len, out_tokens, verify_len_out, lse_target=None, lse_draft=None, survival=None,
               residual_mass=None, sampled_prob=None, rows_read=None, device_status=None,
-              draft_mode: int = SV_DRAFT_PROBS) -> Args:
+              draft_mode: int = SV_DRAFT_PROBS, target_row_offsets=None, draft_row_offsets=None) -> Args:
     """Fill an Args struct.  Strides are (batch, row) in elements."""
     return Args(
         B, K, _addr(target), int(target_strides[0]), int(target_strides[1]),
@@ -134,7 +135,8 @@ def make_args(B: int, K: int, *, target, draft=None, tokens, uniforms=None, temp
         _addr(verify_len), _addr(confidence), _addr(tau),
         _addr(accepted_len), _addr(out_tokens), _addr(verify_len_out),
         _addr(lse_target), _addr(lse_draft), _addr(survival), _addr(residual_mass), _addr(sampled_prob),
-        _addr(rows_read), _addr(device_status), int(draft_mode))
+        _addr(rows_read), _addr(device_status), int(draft_mode), _addr(target_row_offsets),
+        _addr(draft_row_offsets))
 
 
 def check(cfg: Config, args: Args) -> int:

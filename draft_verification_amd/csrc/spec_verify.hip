@@ -108,6 +108,8 @@ struct Params {
     int B, K, V, nsplit, seg_w;   // seg_w: the power of two >= nsplit
     int greedy, derived;       // derived: tau mode with c = max draft probability
     int onehot;                // q_j is the point mass at x_j; no draft row is streamed
+    const long long* toff;     // packed rows: target rows of sequence b start at row toff[b] (NULL: dense)
+    const long long* doff;     // packed rows: draft rows of sequence b start at row doff[b]
     int len_mode;
     const void* t;
     long long tbs, trs;
@@ -369,6 +371,20 @@ __device__ __forceinline__ const void* row_ptr(const void* base, long long bs, l
     return (const void*)((const char*)base + off * (DT == SV_BF16 ? 2 : 4));
 }
 
+// Row j (0-based) of sequence b, dense ([B][rows][V] by strides) or packed
+// (the sequence's rows start at row off[b] of a [sum of rows][V] tensor).
+template <int DT>
+__device__ __forceinline__ const void* seq_row(const void* base, const long long* off, long long bs, long long rs, int b,
+                                               int j)
+{
+    if (off) {
+        typedef const __attribute__((address_space(4))) long long* cptr;
+        const long long r = ((cptr)off)[b] + j; // uniform: a scalar load
+        return (const void*)((const char*)base + r * rs * (DT == SV_BF16 ? 2 : 4));
+    }
+    return row_ptr<DT>(base, bs, rs, b, j);
+}
+
 // exp2((l - m) * c) with c = c_hi + c_lo; exact subtraction for bf16 inputs,
 // no bias from rounding c.  l = -inf gives 0 (c_lo > 0 keeps the product -inf).
 __device__ __forceinline__ float scaled_exp2(float l, float m, float c_hi, float c_lo)
@@ -496,7 +512,13 @@ __global__ __launch_bounds__(kThreads) void sv_plan_kernel(Params p, Work w)
     st.pad = 0;
     bool bad = false, len_open = false;
     int L;
-    if (p.len_mode == SV_LEN_FIXED) {
+    if (p.toff) {
+        // packed rows: the sequence brings L + 1 target rows (and L draft rows)
+        const long long nt = p.toff[b + 1] - p.toff[b];
+        L = (int)(nt - 1);
+        if (nt < 1 || nt > K + 1) bad = true;
+        if (p.doff && p.doff[b + 1] - p.doff[b] != nt - 1) bad = true;
+    } else if (p.len_mode == SV_LEN_FIXED) {
         L = p.vl_in ? p.vl_in[b] : K;
         if (L < 0 || L > K) bad = true;
     } else if (p.conf) {
@@ -560,7 +582,7 @@ template <int DT>
 __device__ __forceinline__ RowRef row_ref(const Params& p, int b, int j, bool draft, int split)
 {
     RowRef r;
-    r.row = draft ? row_ptr<DT>(p.d, p.dbs, p.drs, b, j - 1) : row_ptr<DT>(p.t, p.tbs, p.trs, b, j - 1);
+    r.row = draft ? seq_row<DT>(p.d, p.doff, p.dbs, p.drs, b, j - 1) : seq_row<DT>(p.t, p.toff, p.tbs, p.trs, b, j - 1);
     r.b = b;
     r.j = j;
     r.prow = draft ? p.K + j : j - 1;
@@ -964,7 +986,7 @@ __global__ __launch_bounds__(kThreads) void sv_resid_kernel(Params p, Work w)
     const SeqState st = w.st[b];
     const DrawCtx c = make_ctx(st, p);
     Chunk<DT> tc, dc;
-    tc.template load<VEC>(row_ptr<DT>(p.t, p.tbs, p.trs, b, st.js - 1), split * kSplit, p.V, threadIdx.x);
+    tc.template load<VEC>(seq_row<DT>(p.t, p.toff, p.tbs, p.trs, b, st.js - 1), split * kSplit, p.V, threadIdx.x);
     if (p.onehot) {
         // the one-hot draft row, built in registers: logit 0 at the drafted
         // token (held by one lane of one split), -inf elsewhere
@@ -978,7 +1000,7 @@ __global__ __launch_bounds__(kThreads) void sv_resid_kernel(Params p, Work w)
         }
         dc.one_hot(e);
     } else {
-        dc.template load<VEC>(row_ptr<DT>(p.d, p.dbs, p.drs, b, st.js - 1), split * kSplit, p.V, threadIdx.x);
+        dc.template load<VEC>(seq_row<DT>(p.d, p.doff, p.dbs, p.drs, b, st.js - 1), split * kSplit, p.V, threadIdx.x);
     }
     split_segments<DT>(tc, dc, c, true, s_seg);
     __syncthreads();
@@ -1063,8 +1085,8 @@ __global__ __launch_bounds__(kThreads) void sv_draw_kernel(Params p, Work w)
         const bool resid = s_resid != 0;
         const int ks = s_split;
         const DrawCtx c = make_ctx(st, p);
-        const void* trow = row_ptr<DT>(p.t, p.tbs, p.trs, b, st.js - 1);
-        const void* drow = (resid && !p.onehot) ? row_ptr<DT>(p.d, p.dbs, p.drs, b, st.js - 1) : nullptr;
+        const void* trow = seq_row<DT>(p.t, p.toff, p.tbs, p.trs, b, st.js - 1);
+        const void* drow = (resid && !p.onehot) ? seq_row<DT>(p.d, p.doff, p.dbs, p.drs, b, st.js - 1) : nullptr;
         const int xone = (resid && p.onehot) ? p.tok[(long long)b * K + (st.js - 1)] : -1; // one-hot draft token
 
         // 2. segment sums of that split: stored by sv_resid for a replacement,
@@ -1415,6 +1437,12 @@ int spec_verify_check(const spec_verify_config* cfg, const spec_verify_args* a)
     if (!a->target_logits || a->target_row_stride < V || a->target_batch_stride < 0) return SV_EINVAL;
     if (!a->draft_tokens) return SV_EINVAL;
     if (a->draft_mode != SV_DRAFT_PROBS && a->draft_mode != SV_DRAFT_ONEHOT) return SV_EINVAL;
+    if (a->draft_row_offsets && !a->target_row_offsets) return SV_EINVAL;
+    if (a->target_row_offsets) {
+        // packed rows: the row counts give L, so the length is fixed and not passed
+        if (a->length_mode != SV_LEN_FIXED || a->verify_len_in) return SV_EINVAL;
+        if (T > 0.0f && a->draft_mode == SV_DRAFT_PROBS && !a->draft_row_offsets) return SV_EINVAL;
+    }
     if (T > 0.0f) {
         if (!a->uniforms) return SV_EINVAL;
         if (a->draft_mode == SV_DRAFT_PROBS) {
@@ -1619,6 +1647,8 @@ int spec_verify_run(spec_verify_t* h, const spec_verify_args* a, void* hip_strea
     p.len_mode = a->length_mode;
     p.derived = (a->length_mode == SV_LEN_TAU && !a->confidence) ? 1 : 0;
     p.onehot = (!greedy && a->draft_mode == SV_DRAFT_ONEHOT) ? 1 : 0;
+    p.toff = (const long long*)a->target_row_offsets;
+    p.doff = (greedy || p.onehot) ? nullptr : (const long long*)a->draft_row_offsets;
     p.t = a->target_logits;
     p.tbs = a->target_batch_stride;
     p.trs = a->target_row_stride;

@@ -53,6 +53,8 @@ class DeviceProblem:
     rows_read: Optional[torch.Tensor] = None
     device_status: Optional[torch.Tensor] = None
     draft_mode: int = B.SV_DRAFT_PROBS
+    target_row_offsets: Optional[torch.Tensor] = None  # packed rows: [B+1] int64
+    draft_row_offsets: Optional[torch.Tensor] = None
 
     @staticmethod
     def upload(target: np.ndarray, draft: Optional[np.ndarray], tokens: np.ndarray,
@@ -101,7 +103,8 @@ class DeviceProblem:
             accepted_len=self.accepted_len, out_tokens=self.out_tokens, verify_len_out=self.verify_len_out,
             lse_target=self.lse_target, lse_draft=self.lse_draft, survival=self.survival,
             residual_mass=self.residual_mass, sampled_prob=self.sampled_prob, rows_read=self.rows_read,
-            device_status=self.device_status, draft_mode=self.draft_mode)
+            device_status=self.device_status, draft_mode=self.draft_mode,
+            target_row_offsets=self.target_row_offsets, draft_row_offsets=self.draft_row_offsets)
 
     def fetch(self) -> dict:
         torch.cuda.synchronize()
@@ -121,6 +124,44 @@ def from_problem(prob, diagnostics: bool = True, device="cuda:0") -> DeviceProbl
                                 length_mode=w.length_mode, verify_len=prob.verify_len,
                                 confidence=prob.confidence, tau=prob.tau, diagnostics=diagnostics, device=device,
                                 draft_mode=getattr(w, "draft_mode", B.SV_DRAFT_PROBS))
+
+
+def packed_from_problem(prob, lengths: Optional[np.ndarray] = None, diagnostics: bool = True,
+                        device="cuda:0") -> DeviceProblem:
+    """Upload a ``synth.Problem`` in the packed ("pruned, not padded") layout:
+    sequence b brings its first L_b + 1 target rows and L_b draft rows, stacked
+    in sequence order, with row offsets.  ``lengths`` (default: the problem's
+    fixed verify lengths, else K) gives L_b; a count outside the valid range is
+    passed through as given (the library marks such a sequence bad)."""
+    w = prob.w
+    Bn, K = prob.tokens.shape
+    if lengths is None:
+        lengths = prob.verify_len if prob.verify_len is not None else np.full(Bn, K, np.int32)
+    lengths = np.asarray(lengths, dtype=np.int64)
+    toff = np.concatenate([[0], np.cumsum(lengths + 1)]).astype(np.int64)
+    doff = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    V = prob.target.shape[-1]
+    # rows a sequence declares beyond the dense tensor's K + 1 repeat its last row
+    tp = np.concatenate([prob.target[b, np.minimum(np.arange(max(int(lengths[b]) + 1, 0)), K)] for b in range(Bn)]
+                        + [np.zeros((0, V), prob.target.dtype)])
+    dp_rows = None
+    if prob.draft is not None:
+        dp_rows = np.concatenate([prob.draft[b, np.minimum(np.arange(max(int(lengths[b]), 0)), K - 1)]
+                                  for b in range(Bn)] + [np.zeros((0, V), prob.draft.dtype)])
+    tp = np.ascontiguousarray(tp if tp.shape[0] else np.zeros((1, V), prob.target.dtype))
+    if dp_rows is not None:
+        dp_rows = np.ascontiguousarray(dp_rows if dp_rows.shape[0] else np.zeros((1, V), prob.draft.dtype))
+    if w.dtype == BF16:
+        tp = tp.view(np.int16)
+        dp_rows = None if dp_rows is None else dp_rows.view(np.int16)
+    d = DeviceProblem(Bn, K, V, w.dtype, float(w.temperature), B.SV_LEN_FIXED,
+                      _dev(tp, device), _dev(dp_rows, device), _dev(prob.tokens.astype(np.int32), device),
+                      _dev(prob.uniforms if w.temperature > 0 else None, device), None, None, None, (0, V), (0, V))
+    d.draft_mode = int(getattr(w, "draft_mode", B.SV_DRAFT_PROBS))
+    d.target_row_offsets = _dev(toff, device)
+    d.draft_row_offsets = _dev(doff, device) if dp_rows is not None else None
+    d.alloc_outputs(diagnostics, device)
+    return d
 
 
 def handle_for(dp: DeviceProblem, device: int = 0, max_batch: Optional[int] = None,

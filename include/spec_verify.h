@@ -145,6 +145,17 @@ typedef struct {
                                       p_j(x_j); the replacement is p_j without x_j, renormalised;
                                       derived c_j = 1.  draft_logits is not read (may be NULL);
                                       lse_draft is not written; no draft row is streamed. */
+    const int64_t* target_row_offsets; /* optional device [B+1]: packed rows ("pruned, not padded":
+                                      zhichai.net article, "Under the hood", on variable-length
+                                      verification in SGLang).  Target row j (0-based) of sequence b
+                                      is row target_row_offsets[b] + j of a [total rows][V] tensor at
+                                      target_logits (row stride as above; batch stride unused); the
+                                      sequence brings L_b + 1 rows, so L_b is their count minus 1
+                                      (SV_LEN_FIXED, verify_len_in must be NULL).  A count outside
+                                      [1, K+1] marks the sequence bad.  NULL = the dense layout. */
+    const int64_t* draft_row_offsets;  /* packed draft rows, [B+1] likewise (L_b rows per sequence;
+                                      a different count marks the sequence bad).  Required with
+                                      target_row_offsets when T > 0 and SV_DRAFT_PROBS. */
 } spec_verify_args;
 
 /* Allocate a handle and its workspace on cfg->device.  *out is set only on SV_OK. */
