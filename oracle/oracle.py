@@ -217,3 +217,57 @@ def schedule(confidence: np.ndarray, speed: np.ndarray) -> ScheduleResult:
     if rc != 0:
         raise ValueError(f"svo_schedule failed ({rc})")
     return ScheduleResult(vl, surv, int(adm[0]), float(tau[0]), float(exp_[0]), bool(mar[0]), bool(bad[0]))
+
+
+def calibrated_confidence_steps(logits_steps, temperature, delay: int, c_default: float, resets=None):
+    """Calibrated, causally delayed confidences over a sequence of steps.
+
+    umans.ai blog, section "2. Verify smarter": raw confidence gets a
+    per-position temperature fitted on held-out data, and the production
+    version sizes the truncation from confidence measured two steps earlier (a
+    causal barrier between the decision and the tokens); zhichai.net article,
+    section "Under the hood": Sequential Temperature Scaling.
+
+    Reading (listed in the design notes): at each step the calibrated
+    confidence of position j is sigmoid(z_j / T_j), in fp64, rounded to fp32
+    (a temperature that is not finite and positive gives 0 and flags bad
+    input); the value handed to the length decision is the calibrated value
+    of the same slot and position from ``delay`` steps earlier, or
+    ``c_default`` while the slot has fewer than ``delay`` earlier steps since
+    its last reset (a new sequence in the slot); delay 0 hands over the
+    current value.
+
+    logits_steps: list of [B][K] arrays (one per step, in order);
+    temperature: [K]; resets: list of [B] bool arrays (or None).
+    Returns (now, out, bad): lists of [B][K] float32 arrays and of bools."""
+    T = np.asarray(temperature, dtype=np.float64)
+    Bn, K = np.asarray(logits_steps[0]).shape
+    history = [[] for _ in range(Bn)]          # calibrated rows of each slot since its reset
+    nows, outs, bads = [], [], []
+    for t, z in enumerate(logits_steps):
+        z = np.asarray(z, dtype=np.float32).astype(np.float64)
+        now = np.empty((Bn, K), np.float32)
+        bad = False
+        for b in range(Bn):
+            for j in range(K):
+                if not (np.isfinite(T[j]) and T[j] > 0.0):
+                    bad = True
+                    now[b, j] = 0.0
+                else:
+                    with np.errstate(over="ignore"):  # exp(+large) = inf gives 0 exactly
+                        now[b, j] = np.float32(1.0 / (1.0 + np.exp(-z[b, j] / T[j])))
+        out = np.empty((Bn, K), np.float32)
+        for b in range(Bn):
+            if resets is not None and resets[t] is not None and resets[t][b]:
+                history[b] = []
+            if delay == 0:
+                out[b] = now[b]
+            elif len(history[b]) >= delay:
+                out[b] = history[b][-delay]
+            else:
+                out[b] = np.float32(c_default)
+            history[b].append(now[b].copy())
+        nows.append(now)
+        outs.append(out)
+        bads.append(bad)
+    return nows, outs, bads
