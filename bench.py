@@ -206,6 +206,28 @@ def time_packed(torch, B, D, synth, steps, warmup):
     return out
 
 
+def time_confidence(sv, torch, B, synth, Bn, K, steps, warmup):
+    """Time one step of calibrated, causally delayed confidences
+    (spec_verify_confidence, delay 2) on the same batch shape."""
+    dev = torch.device("cuda")
+    z = torch.from_numpy((4.0 * synth.uniforms(600, Bn * K) - 2.0).reshape(Bn, K)).to(dev)
+    T = torch.from_numpy(np.linspace(0.8, 1.6, K).astype(np.float32)).to(dev)
+    out = torch.empty((Bn, K), dtype=torch.float32, device=dev)
+    a = B.make_conf_args(Bn, K, conf_logits=z, temperature=T, conf_out=out, delay=2, c_default=0.0)
+    stream = torch.cuda.current_stream().cuda_stream
+    for _ in range(max(warmup, 3)):
+        sv.confidence(a, stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        sv.confidence(a, stream)
+    e1.record()
+    torch.cuda.synchronize()
+    return {"us_per_call": e0.elapsed_time(e1) / steps * 1e3, "B": Bn, "K": K, "delay": 2,
+            "inputs": "logits uniform in [-2, 2) (Philox key 600), temperatures 0.8 .. 1.6"}
+
+
 def time_admission(sv, torch, B, synth, Bn, K, steps, warmup):
     """Time the load-aware admission decision (spec_verify_schedule) on the
     same batch shape: seeded confidences and a linear step-time curve."""
@@ -308,6 +330,7 @@ def main():
     kms, nruns = sv.timing_end()
     kernel_avg_ms = {k: v / max(nruns, 1) for k, v in kms.items()}
     admission = time_admission(sv, torch, B, synth, w.B, w.K, args.steps, args.warmup)
+    confidence = time_confidence(sv, torch, B, synth, w.B, w.K, args.steps, args.warmup)
     sv.close()
     del dps, argv
     onehot = time_onehot(torch, B, D, synth, args.steps, args.warmup)
@@ -359,6 +382,7 @@ def main():
         "kernel_avg_ms": kernel_avg_ms,
         "kernel_src_sha": src_hash,
         "admission": admission,
+        "confidence": confidence,
         "onehot": onehot,
         "packed": packed,
     }

@@ -24,7 +24,9 @@ EXPORTED = (
     "spec_verify_create", "spec_verify_check", "spec_verify_run", "spec_verify_destroy",
     "spec_verify_status_string", "spec_verify_timing_begin", "spec_verify_timing_end",
     "spec_verify_kernel_count", "spec_verify_kernel_name", "spec_verify_sched_check", "spec_verify_schedule",
+    "spec_verify_conf_check", "spec_verify_confidence",
 )
+SV_MAX_CONF_DELAY = 4
 SV_MAX_SCHED_BATCH, SV_MAX_SCHED_CANDIDATES = 4096, 65536
 
 
@@ -56,6 +58,15 @@ class SchedArgs(ctypes.Structure):
         ("B", ctypes.c_int32), ("K", ctypes.c_int32), ("confidence", ctypes.c_void_p), ("speed", ctypes.c_void_p),
         ("n_speed", ctypes.c_int32), ("verify_len_out", ctypes.c_void_p), ("survival", ctypes.c_void_p),
         ("admitted", ctypes.c_void_p), ("tau", ctypes.c_void_p), ("expected_rate", ctypes.c_void_p),
+        ("device_status", ctypes.c_void_p),
+    ]
+
+
+class ConfArgs(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int32), ("K", ctypes.c_int32), ("conf_logits", ctypes.c_void_p),
+        ("temperature", ctypes.c_void_p), ("reset", ctypes.c_void_p), ("delay", ctypes.c_int32),
+        ("c_default", ctypes.c_float), ("conf_now", ctypes.c_void_p), ("conf_out", ctypes.c_void_p),
         ("device_status", ctypes.c_void_p),
     ]
 
@@ -99,6 +110,10 @@ def lib() -> ctypes.CDLL:
         L.spec_verify_sched_check.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(SchedArgs)]
         L.spec_verify_schedule.restype = ctypes.c_int
         L.spec_verify_schedule.argtypes = [ctypes.c_void_p, ctypes.POINTER(SchedArgs), ctypes.c_void_p]
+        L.spec_verify_conf_check.restype = ctypes.c_int
+        L.spec_verify_conf_check.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(ConfArgs)]
+        L.spec_verify_confidence.restype = ctypes.c_int
+        L.spec_verify_confidence.argtypes = [ctypes.c_void_p, ctypes.POINTER(ConfArgs), ctypes.c_void_p]
         _lib = L
     return _lib
 
@@ -151,6 +166,18 @@ def make_sched_args(B: int, K: int, *, confidence, speed, n_speed: int, verify_l
                      _addr(admitted), _addr(tau), _addr(expected_rate), _addr(device_status))
 
 
+def make_conf_args(B: int, K: int, *, conf_logits, temperature, conf_out, delay: int = 2, c_default: float = 0.0,
+                   reset=None, conf_now=None, device_status=None) -> ConfArgs:
+    """Fill a ConfArgs struct (device tensors or addresses)."""
+    return ConfArgs(B, K, _addr(conf_logits), _addr(temperature), _addr(reset), int(delay), float(c_default),
+                    _addr(conf_now), _addr(conf_out), _addr(device_status))
+
+
+def conf_check(cfg: Config, args: ConfArgs) -> int:
+    """Host-only check of a confidence call (no device work)."""
+    return int(lib().spec_verify_conf_check(ctypes.byref(cfg), ctypes.byref(args)))
+
+
 def sched_check(cfg: Config, args: SchedArgs) -> int:
     """Host-only check of an admission call (no device work)."""
     return int(lib().spec_verify_sched_check(ctypes.byref(cfg), ctypes.byref(args)))
@@ -184,6 +211,15 @@ class SpecVerify:
         rc = lib().spec_verify_schedule(self._h, ctypes.byref(args), ctypes.c_void_p(stream))
         if rc != SV_OK:
             raise SpecVerifyError(rc, "spec_verify_schedule")
+
+    def confidence(self, args: ConfArgs, stream: Optional[int] = None) -> None:
+        """Enqueue one step of calibrated, delayed confidences on ``stream``."""
+        if stream is None:
+            import torch
+            stream = torch.cuda.current_stream(self.cfg.device).cuda_stream
+        rc = lib().spec_verify_confidence(self._h, ctypes.byref(args), ctypes.c_void_p(stream))
+        if rc != SV_OK:
+            raise SpecVerifyError(rc, "spec_verify_confidence")
 
     def timing_begin(self, max_calls: int) -> None:
         rc = lib().spec_verify_timing_begin(self._h, int(max_calls))

@@ -69,8 +69,12 @@ constexpr int kSplit = 16384;                     // elements per split (fixed f
 constexpr int kPerLane = kSplit / kThreads;       // 64 elements per lane per split
 constexpr int kMaxGroup = 16;                     // positions per group
 
-enum { CTL_STATUS = 0, CTL_SCHED_STATUS = 1, CTL_WORDS = 64 };
+enum { CTL_STATUS = 0, CTL_SCHED_STATUS = 1, CTL_CONF_STATUS = 2, CTL_WORDS = 64 };
 enum { FL_ACC = 1, FL_LEN = 2 };
+// Compile-time variants of the step kernels: MODE_ONEHOT (q is the point mass
+// at the drafted token; never with greedy verification) and MODE_PACKED (rows
+// addressed through per-sequence offsets).
+enum { MODE_ONEHOT = 1, MODE_PACKED = 2 };
 enum { KIND_NONE = -1, KIND_RESID = 0, KIND_BONUS = 1, KIND_GREEDY = 2, KIND_BAD = 3 };
 enum { K_PLAN = 0, K_ROWS = 1, K_DECIDE = 2, K_RESID = 3, K_DRAW = 4, K_COUNT = 5 };
 
@@ -99,9 +103,19 @@ struct Work {
     double* rsum;     // [max_batch][nsplit] residual mass per split
     double* seg;      // [max_batch][nsplit][64] residual mass per segment of a split
     float* xlog;      // [max_batch][2K+1] logit of the drafted token in each row
-    double* sched_s;  // [B][K] survivals of the admission scheduler
-    int* sched_rank;  // [B][K] rank of each drafted position by survival
+};
+
+// Workspace of the admission and confidence calls (kept out of Work so that the
+// verify kernels' arguments stay small).
+struct AuxWork {
+    int* ctl;
+    double* sched_s;      // [B][K] survivals of the admission scheduler
+    int* sched_rank;      // [B][K] rank of each drafted position by survival
     double* sched_sorted; // [B K] survivals in rank order
+    float* conf_ring;     // [max_batch][SV_MAX_CONF_DELAY][max_draft] calibrated confidences of past calls
+    int* conf_head;       // [max_batch] ring slot of the next call
+    int* conf_count;      // [max_batch] calls recorded since the slot's reset (capped)
+    int conf_K;           // max_draft: the ring's row length
 };
 
 struct Params {
@@ -373,11 +387,11 @@ __device__ __forceinline__ const void* row_ptr(const void* base, long long bs, l
 
 // Row j (0-based) of sequence b, dense ([B][rows][V] by strides) or packed
 // (the sequence's rows start at row off[b] of a [sum of rows][V] tensor).
-template <int DT>
+template <int DT, bool PK>
 __device__ __forceinline__ const void* seq_row(const void* base, const long long* off, long long bs, long long rs, int b,
                                                int j)
 {
-    if (off) {
+    if (PK) {
         typedef const __attribute__((address_space(4))) long long* cptr;
         const long long r = ((cptr)off)[b] + j; // uniform: a scalar load
         return (const void*)((const char*)base + r * rs * (DT == SV_BF16 ? 2 : 4));
@@ -578,11 +592,12 @@ struct RowRef {
     int b, j, prow, split;
 };
 
-template <int DT>
+template <int DT, bool PK>
 __device__ __forceinline__ RowRef row_ref(const Params& p, int b, int j, bool draft, int split)
 {
     RowRef r;
-    r.row = draft ? seq_row<DT>(p.d, p.doff, p.dbs, p.drs, b, j - 1) : seq_row<DT>(p.t, p.toff, p.tbs, p.trs, b, j - 1);
+    r.row = draft ? seq_row<DT, PK>(p.d, p.doff, p.dbs, p.drs, b, j - 1)
+                  : seq_row<DT, PK>(p.t, p.toff, p.tbs, p.trs, b, j - 1);
     r.b = b;
     r.j = j;
     r.prow = draft ? p.K + j : j - 1;
@@ -640,17 +655,18 @@ __device__ __forceinline__ void rows_finish(const Params& p, const Work& w, cons
 // consecutive workgroups stream consecutive 32 KB pieces of a row (HBM keeps
 // its rate on long contiguous runs).  A workgroup of a row the walk does not
 // need exits after one scalar load.
-template <int DT, bool VEC, bool GREEDY>
+template <int DT, bool VEC, bool GREEDY, int MODE>
 __global__ __launch_bounds__(kThreads, (DT == SV_BF16 && VEC) ? 8 : 1) void sv_rows_kernel(Params p, Work w, int j0,
                                                                                            int G)
 {
+    constexpr bool OH = (MODE & MODE_ONEHOT) != 0, PK = (MODE & MODE_PACKED) != 0;
     __shared__ float redf[kWaves];
     __shared__ double redd[kWaves];
     __shared__ int redi[kWaves];
     const int t = (int)threadIdx.x;
     const int split = (int)(blockIdx.x % (unsigned)p.nsplit);
     const int rest = (int)(blockIdx.x / (unsigned)p.nsplit);
-    const int slots = (GREEDY || p.onehot) ? G : 2 * G; // one-hot drafts: target rows only
+    const int slots = (GREEDY || OH) ? G : 2 * G; // one-hot drafts: target rows only
     const int slot = rest % slots;
     const int b = rest / slots;
     const bool draft = !GREEDY && slot >= G;
@@ -660,7 +676,7 @@ __global__ __launch_bounds__(kThreads, (DT == SV_BF16 && VEC) ? 8 : 1) void sv_r
     const int flags = lv & 3, L = (lv >> 2) - 1;
     const bool need = draft ? draft_row_needed(flags, L, j, p.K) : target_row_needed(flags, L, j, p.K);
     if (!need) return;
-    const RowRef r = row_ref<DT>(p, b, j, draft, split);
+    const RowRef r = row_ref<DT, PK>(p, b, j, draft, split);
     Chunk<DT> c;
     c.template issue<VEC>(r.row, split * kSplit, p.V, t);
     c.template fix_tail<VEC>(split * kSplit, p.V, t);
@@ -696,9 +712,10 @@ __device__ __forceinline__ void seg_argmax(float& v, int& i, int sw)
     }
 }
 
-template <int DT, bool GREEDY>
+template <int DT, bool GREEDY, int MODE>
 __global__ __launch_bounds__(kThreads) void sv_decide_kernel(Params p, Work w, int j0, int G)
 {
+    constexpr bool OH = (MODE & MODE_ONEHOT) != 0;
     __shared__ float sMt[kMaxGroup], sMd[kMaxGroup], sLt[kMaxGroup], sLd[kMaxGroup];
     __shared__ double sSt[kMaxGroup], sSd[kMaxGroup];
     __shared__ int sG[kMaxGroup];
@@ -714,7 +731,7 @@ __global__ __launch_bounds__(kThreads) void sv_decide_kernel(Params p, Work w, i
         const int t = base + tid;
         const int pk = t / sw, k = t % sw;
         const int q = pk >> 1, kind = pk & 1, j = j0 + q;
-        const bool read = t < per && (kind ? (!GREEDY && !p.onehot && draft_row_needed(flags0, L0, j, K))
+        const bool read = t < per && (kind ? (!GREEDY && !OH && draft_row_needed(flags0, L0, j, K))
                                            : target_row_needed(flags0, L0, j, K));
         const bool has = read && k < p.nsplit;
         const long long pi = has ? part_index(p, b, kind ? K + j : j - 1) + k : 0;
@@ -742,7 +759,7 @@ __global__ __launch_bounds__(kThreads) void sv_decide_kernel(Params p, Work w, i
         if (kind < 2 && q < n && j <= K) {
             const bool read = kind ? draft_row_needed(flags0, L0, j, K) : target_row_needed(flags0, L0, j, K);
             if (read) {
-                if (kind && p.onehot) {
+                if (kind && OH) {
                     // the one-hot draft row: logit 0 at x, -inf elsewhere (max 0, sum 1)
                     sLd[q] = 0.0f;
                     sMd[q] = 0.0f;
@@ -773,7 +790,7 @@ __global__ __launch_bounds__(kThreads) void sv_decide_kernel(Params p, Work w, i
                 sRatio[q] = ratio;
             }
             if (tread && p.lse_t) sLseT[q] = (float)((double)sMt[q] * p.invT64 + log(sSt[q]));
-            if (dread && p.lse_d && !p.onehot) sLseD[q] = (float)((double)sMd[q] * p.invT64 + log(sSd[q]));
+            if (dread && p.lse_d && !OH) sLseD[q] = (float)((double)sMd[q] * p.invT64 + log(sSd[q]));
         }
     }
     __syncthreads();
@@ -785,12 +802,12 @@ __global__ __launch_bounds__(kThreads) void sv_decide_kernel(Params p, Work w, i
     for (int q = 0; q < n; ++q) {
         const int j = j0 + q;
         const bool dread = !GREEDY && draft_row_needed(flags0, L0, j, K);
-        st.rows += (target_row_needed(flags0, L0, j, K) ? 1 : 0) + ((dread && !p.onehot) ? 1 : 0);
+        st.rows += (target_row_needed(flags0, L0, j, K) ? 1 : 0) + ((dread && !OH) ? 1 : 0);
         if (!acc && !len) continue; // rows of this group past the stop were still streamed
         if (!GREEDY) {
             if (acc && p.lse_t) p.lse_t[(long long)b * (K + 1) + (j - 1)] = sLseT[q];
-            if (dread && p.lse_d && !p.onehot) p.lse_d[(long long)b * K + (j - 1)] = sLseD[q];
-            if (dread && p.derived && !p.onehot) {
+            if (dread && p.lse_d && !OH) p.lse_d[(long long)b * K + (j - 1)] = sLseD[q];
+            if (dread && p.derived && !OH) {
                 // c_j = max_v q_j(v) = 1 / Sd; S_j = S_{j-1} c_j
                 const double S = st.S / sSd[q];
                 st.S = S;
@@ -975,9 +992,10 @@ __device__ __forceinline__ void split_segments(const Chunk<DT>& tc, const Chunk<
     }
 }
 
-template <int DT, bool VEC>
+template <int DT, bool VEC, int MODE>
 __global__ __launch_bounds__(kThreads) void sv_resid_kernel(Params p, Work w)
 {
+    constexpr bool OH = (MODE & MODE_ONEHOT) != 0, PK = (MODE & MODE_PACKED) != 0;
     using S = Seg<DT>;
     __shared__ double s_seg[S::SEGS];
     const int b = (int)(blockIdx.x / p.nsplit);
@@ -986,8 +1004,8 @@ __global__ __launch_bounds__(kThreads) void sv_resid_kernel(Params p, Work w)
     const SeqState st = w.st[b];
     const DrawCtx c = make_ctx(st, p);
     Chunk<DT> tc, dc;
-    tc.template load<VEC>(seq_row<DT>(p.t, p.toff, p.tbs, p.trs, b, st.js - 1), split * kSplit, p.V, threadIdx.x);
-    if (p.onehot) {
+    tc.template load<VEC>(seq_row<DT, PK>(p.t, p.toff, p.tbs, p.trs, b, st.js - 1), split * kSplit, p.V, threadIdx.x);
+    if (OH) {
         // the one-hot draft row, built in registers: logit 0 at the drafted
         // token (held by one lane of one split), -inf elsewhere
         const int x = p.tok[(long long)b * p.K + (st.js - 1)];
@@ -1000,7 +1018,7 @@ __global__ __launch_bounds__(kThreads) void sv_resid_kernel(Params p, Work w)
         }
         dc.one_hot(e);
     } else {
-        dc.template load<VEC>(seq_row<DT>(p.d, p.doff, p.dbs, p.drs, b, st.js - 1), split * kSplit, p.V, threadIdx.x);
+        dc.template load<VEC>(seq_row<DT, PK>(p.d, p.doff, p.dbs, p.drs, b, st.js - 1), split * kSplit, p.V, threadIdx.x);
     }
     split_segments<DT>(tc, dc, c, true, s_seg);
     __syncthreads();
@@ -1036,9 +1054,10 @@ __device__ __forceinline__ int wave_last_positive(double v, int n)
     return pos ? 63 - __clzll(pos) : -1;
 }
 
-template <int DT, bool VEC>
+template <int DT, bool VEC, int MODE>
 __global__ __launch_bounds__(kThreads) void sv_draw_kernel(Params p, Work w)
 {
+    constexpr bool OH = (MODE & MODE_ONEHOT) != 0, PK = (MODE & MODE_PACKED) != 0;
     using S = Seg<DT>;
     __shared__ double s_seg[S::SEGS];
     __shared__ double s_wrel, s_Z, s_my;
@@ -1085,9 +1104,9 @@ __global__ __launch_bounds__(kThreads) void sv_draw_kernel(Params p, Work w)
         const bool resid = s_resid != 0;
         const int ks = s_split;
         const DrawCtx c = make_ctx(st, p);
-        const void* trow = seq_row<DT>(p.t, p.toff, p.tbs, p.trs, b, st.js - 1);
-        const void* drow = (resid && !p.onehot) ? seq_row<DT>(p.d, p.doff, p.dbs, p.drs, b, st.js - 1) : nullptr;
-        const int xone = (resid && p.onehot) ? p.tok[(long long)b * K + (st.js - 1)] : -1; // one-hot draft token
+        const void* trow = seq_row<DT, PK>(p.t, p.toff, p.tbs, p.trs, b, st.js - 1);
+        const void* drow = (resid && !OH) ? seq_row<DT, PK>(p.d, p.doff, p.dbs, p.drs, b, st.js - 1) : nullptr;
+        const int xone = (resid && OH) ? p.tok[(long long)b * K + (st.js - 1)] : -1; // one-hot draft token
 
         // 2. segment sums of that split: stored by sv_resid for a replacement,
         //    computed here for a bonus draw
@@ -1115,7 +1134,7 @@ __global__ __launch_bounds__(kThreads) void sv_draw_kernel(Params p, Work w)
             for (int i = 0; i < S::RUN; ++i) {
                 lt[i] = i0 + i < p.V ? load_one<DT>(trow, i0 + i) : -INFINITY;
                 ld[i] = (resid && i0 + i < p.V)
-                            ? (p.onehot ? (i0 + i == xone ? 0.0f : -INFINITY) : load_one<DT>(drow, i0 + i))
+                            ? (OH ? (i0 + i == xone ? 0.0f : -INFINITY) : load_one<DT>(drow, i0 + i))
                             : -INFINITY;
             }
             bool slow;
@@ -1152,7 +1171,7 @@ __global__ __launch_bounds__(kThreads) void sv_draw_kernel(Params p, Work w)
                 if (yy < 0) yy = lastpos >= 0 ? lastpos : i0; // rounding: last token with mass
                 s_y = yy;
                 // the reported probability of the chosen token is evaluated in fp64
-                const float ldy = !resid ? 0.0f : (p.onehot ? (yy == xone ? 0.0f : -INFINITY) : load_one<DT>(drow, yy));
+                const float ldy = !resid ? 0.0f : (OH ? (yy == xone ? 0.0f : -INFINITY) : load_one<DT>(drow, yy));
                 s_my = mass_f64(load_one<DT>(trow, yy), ldy, c, resid);
             }
         }
@@ -1213,7 +1232,7 @@ struct SchedParams {
 };
 
 // survivals, left to right in fp64, one thread per sequence
-__global__ __launch_bounds__(kThreads) void sv_sched_surv_kernel(SchedParams q, Work w)
+__global__ __launch_bounds__(kThreads) void sv_sched_surv_kernel(SchedParams q, AuxWork w)
 {
     const int b = (int)(blockIdx.x * kThreads + threadIdx.x);
     if (b >= q.B) return;
@@ -1238,7 +1257,7 @@ __global__ __launch_bounds__(kThreads) void sv_sched_surv_kernel(SchedParams q, 
 // every other sequence b', the number of its survivals that rank before S_bj:
 // those > S_bj, and for b' < b also those equal to it (one binary search per
 // sequence).  One workgroup per position, threads over sequences.
-__global__ __launch_bounds__(kThreads) void sv_sched_rank_kernel(SchedParams q, Work w)
+__global__ __launch_bounds__(kThreads) void sv_sched_rank_kernel(SchedParams q, AuxWork w)
 {
     __shared__ double red[kWaves];
     const int i = blockIdx.x;
@@ -1270,7 +1289,7 @@ __global__ __launch_bounds__(kThreads) void sv_sched_rank_kernel(SchedParams q, 
 // fixed order), the first m at which T stops rising, and the outputs.
 constexpr int kSchedThreads = 1024;
 
-__global__ __launch_bounds__(kSchedThreads) void sv_sched_pick_kernel(SchedParams q, Work w)
+__global__ __launch_bounds__(kSchedThreads) void sv_sched_pick_kernel(SchedParams q, AuxWork w)
 {
     __shared__ double s_scan[kSchedThreads];
     __shared__ int s_first[kSchedThreads / 64];
@@ -1330,13 +1349,73 @@ __global__ __launch_bounds__(kSchedThreads) void sv_sched_pick_kernel(SchedParam
     }
 }
 
+// ---------------------------------------------------------------- confidences
+//
+// Calibrated, causally delayed confidences (umans.ai blog, "2. Verify
+// smarter"; zhichai.net article, "Under the hood"): sigmoid(z / T_j) per
+// position, handed over `delay` calls later from a per-slot ring.
+
+struct ConfParams {
+    int B, K, delay;
+    float c_default;
+    const float* z;
+    const float* temp;
+    const int* reset;
+    float* now_out;
+    float* out;
+    int* status_out;
+};
+
+// one workgroup per slot, one thread per position
+__global__ __launch_bounds__(kThreads) void sv_conf_kernel(ConfParams q, AuxWork w)
+{
+    __shared__ int s_h, s_n;
+    const int b = blockIdx.x;
+    if (threadIdx.x == 0) {
+        const bool fresh = q.reset && q.reset[b] != 0;
+        s_h = w.conf_head[b];
+        s_n = fresh ? 0 : w.conf_count[b];
+    }
+    __syncthreads();
+    const int h = s_h, n = s_n;
+    float* ring = w.conf_ring + (long long)b * SV_MAX_CONF_DELAY * w.conf_K;
+    for (int j = threadIdx.x; j < q.K; j += kThreads) {
+        const long long i = (long long)b * q.K + j;
+        const double T = (double)q.temp[j];
+        float now;
+        if (!(T > 0.0 && T < INFINITY)) {
+            now = 0.0f;
+            or_status(&w.ctl[CTL_CONF_STATUS], SV_STATUS_BAD_INPUT);
+        } else {
+            // 1 / (1 + e^{-z/T}); e^{-x} = 2^{-x log2 e} with this library's fp64 exp2
+            const double x = (double)q.z[i] / T;
+            now = (float)(1.0 / (1.0 + exp2_f64(-x * 1.4426950408889634073599246810019)));
+        }
+        float out;
+        if (q.delay == 0) out = now;
+        else if (n >= q.delay) out = ring[((h - q.delay + SV_MAX_CONF_DELAY) % SV_MAX_CONF_DELAY) * w.conf_K + j];
+        else out = q.c_default;
+        ring[h * w.conf_K + j] = now; // after the read: delay SV_MAX_CONF_DELAY reads this entry
+        q.out[i] = out;
+        if (q.now_out) q.now_out[i] = now;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        w.conf_head[b] = (h + 1) % SV_MAX_CONF_DELAY;
+        w.conf_count[b] = min(n + 1, SV_MAX_CONF_DELAY);
+    }
+}
+
+__global__ void sv_conf_status_kernel(ConfParams q, AuxWork w)
+{
+    if (threadIdx.x == 0 && blockIdx.x == 0) {
+        if (q.status_out) *q.status_out = w.ctl[CTL_CONF_STATUS];
+        w.ctl[CTL_CONF_STATUS] = 0;
+    }
+}
+
 // ---------------------------------------------------------------- host side
 
-template <int DT, bool VEC, bool GR>
-void launch_rows(unsigned grid, hipStream_t s, const Params& p, const Work& w, int j0, int G)
-{
-    hipLaunchKernelGGL((sv_rows_kernel<DT, VEC, GR>), dim3(grid), dim3(kThreads), 0, s, p, w, j0, G);
-}
 
 const char* const kKernelNames[K_COUNT] = {"sv_plan", "sv_rows", "sv_decide", "sv_resid", "sv_draw"};
 constexpr int kMaxSlots = 64; // timed launches per run
@@ -1348,12 +1427,51 @@ struct spec_verify {
     int nsplit;
     void* ws;
     Work w;
+    AuxWork aux;
     int timing_max, timing_n;
     hipEvent_t* ev;       // [timing_max][kMaxSlots][2]
     int* ev_kernel;       // [timing_max][kMaxSlots] kernel id of each timed launch, -1 unused
 };
 
 namespace {
+
+// One verification step on stream s: plan, then per position group (2, 2, 4,
+// 8, ...; a remainder of one position joins the previous group) the row
+// statistics and the decisions, then the residual masses and the final draw.
+template <int DT, bool VEC, bool GR, int MODE, typename Mark>
+void enqueue_step(const spec_verify* h, const Params& p, hipStream_t s, Mark& mark)
+{
+    constexpr bool OH = (MODE & MODE_ONEHOT) != 0;
+    const unsigned B = (unsigned)p.B;
+    mark(K_PLAN, 0);
+    hipLaunchKernelGGL(sv_plan_kernel, dim3((B + kThreads - 1) / kThreads), dim3(kThreads), 0, s, p, h->w);
+    mark(K_PLAN, 1);
+    int j0 = 1, gsz = 2;
+    const int npos = p.K + 1;
+    while (j0 <= npos) {
+        int G = gsz;
+        if (npos - (j0 + G - 1) <= 1) G = npos - j0 + 1;
+        if (G > kMaxGroup) G = kMaxGroup;
+        const unsigned grid = (unsigned)((long long)B * ((GR || OH) ? G : 2 * G) * p.nsplit);
+        mark(K_ROWS, 0);
+        hipLaunchKernelGGL((sv_rows_kernel<DT, VEC, GR, MODE>), dim3(grid), dim3(kThreads), 0, s, p, h->w, j0, G);
+        mark(K_ROWS, 1);
+        mark(K_DECIDE, 0);
+        hipLaunchKernelGGL((sv_decide_kernel<DT, GR, MODE & MODE_ONEHOT>), dim3(B), dim3(kThreads), 0, s, p, h->w, j0,
+                           G);
+        mark(K_DECIDE, 1);
+        j0 += G;
+        gsz = gsz < kMaxGroup ? (j0 <= 3 ? 2 : gsz * 2) : kMaxGroup;
+    }
+    mark(K_RESID, 0);
+    if (!GR)
+        hipLaunchKernelGGL((sv_resid_kernel<DT, VEC, MODE>), dim3(B * (unsigned)p.nsplit), dim3(kThreads), 0, s, p,
+                           h->w);
+    mark(K_RESID, 1);
+    mark(K_DRAW, 0);
+    hipLaunchKernelGGL((sv_draw_kernel<DT, VEC, MODE>), dim3(B), dim3(kThreads), 0, s, p, h->w);
+    mark(K_DRAW, 1);
+}
 
 size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -1488,6 +1606,10 @@ int spec_verify_create(const spec_verify_config* cfg, spec_verify_t** out)
     const size_t o_ss = off; off = align_up(off + (size_t)ncand * sizeof(double));
     const size_t o_sr = off; off = align_up(off + (size_t)ncand * sizeof(int));
     const size_t o_so = off; off = align_up(off + (size_t)ncand * sizeof(double));
+    const bool conf_ok = (long long)cfg->max_batch * cfg->max_draft <= SV_MAX_SCHED_CANDIDATES;
+    const size_t o_cr = off; off = align_up(off + (conf_ok ? (size_t)ncand * SV_MAX_CONF_DELAY * sizeof(float) : 0));
+    const size_t o_ch = off; off = align_up(off + (conf_ok ? (size_t)cfg->max_batch * sizeof(int) : 0));
+    const size_t o_cc = off; off = align_up(off + (conf_ok ? (size_t)cfg->max_batch * sizeof(int) : 0));
     if (hipMalloc(&h->ws, off) != hipSuccess) { free(h); return SV_ENOMEM; }
     char* base = (char*)h->ws;
     h->w.ctl = (int*)(base + o_ctl);
@@ -1500,11 +1622,21 @@ int spec_verify_create(const spec_verify_config* cfg, spec_verify_t** out)
     h->w.rsum = (double*)(base + o_rs);
     h->w.seg = (double*)(base + o_sg);
     h->w.xlog = (float*)(base + o_xl);
-    h->w.sched_s = (double*)(base + o_ss);
-    h->w.sched_rank = (int*)(base + o_sr);
-    h->w.sched_sorted = (double*)(base + o_so);
-    // control words (status bits) start at zero; each call clears what it reports
-    if (hipMemset(h->w.ctl, 0, CTL_WORDS * sizeof(int)) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+    h->aux.ctl = h->w.ctl;
+    h->aux.sched_s = (double*)(base + o_ss);
+    h->aux.sched_rank = (int*)(base + o_sr);
+    h->aux.sched_sorted = (double*)(base + o_so);
+    h->aux.conf_ring = conf_ok ? (float*)(base + o_cr) : nullptr;
+    h->aux.conf_head = conf_ok ? (int*)(base + o_ch) : nullptr;
+    h->aux.conf_count = conf_ok ? (int*)(base + o_cc) : nullptr;
+    h->aux.conf_K = cfg->max_draft;
+    // control words (status bits) start at zero; each call clears what it reports;
+    // the confidence history starts empty
+    bool zero_ok = hipMemset(h->w.ctl, 0, CTL_WORDS * sizeof(int)) == hipSuccess;
+    if (conf_ok) {
+        zero_ok = zero_ok && hipMemset(base + o_cr, 0, o_cc + (size_t)cfg->max_batch * sizeof(int) - o_cr) == hipSuccess;
+    }
+    if (!zero_ok || hipDeviceSynchronize() != hipSuccess) {
         (void)hipFree(h->ws);
         free(h);
         return SV_EDEVICE;
@@ -1584,6 +1716,43 @@ int spec_verify_timing_end(spec_verify_t* h, double* ms, int32_t n_kernels, int3
     return rc;
 }
 
+int spec_verify_conf_check(const spec_verify_config* cfg, const spec_verify_conf_args* a)
+{
+    int rc = check_config(cfg);
+    if (rc != SV_OK) return rc;
+    if (!a) return SV_EINVAL;
+    if (a->B < 0 || a->B > cfg->max_batch || a->K < 1 || a->K > cfg->max_draft) return SV_EINVAL;
+    if (a->delay < 0 || a->delay > SV_MAX_CONF_DELAY) return SV_EINVAL;
+    if ((long long)cfg->max_batch * cfg->max_draft > SV_MAX_SCHED_CANDIDATES) return SV_EUNSUPPORTED;
+    if (a->B == 0) return SV_OK;
+    if (!a->conf_logits || !a->temperature || !a->conf_out) return SV_EINVAL;
+    return SV_OK;
+}
+
+int spec_verify_confidence(spec_verify_t* h, const spec_verify_conf_args* a, void* hip_stream)
+{
+    if (!h) return SV_EINVAL;
+    int rc = spec_verify_conf_check(&h->cfg, a);
+    if (rc != SV_OK) return rc;
+    if (a->B == 0) return SV_OK;
+    DeviceGuard guard(h->cfg.device);
+    hipStream_t s = (hipStream_t)hip_stream;
+    ConfParams q;
+    q.B = a->B;
+    q.K = a->K;
+    q.delay = a->delay;
+    q.c_default = a->c_default;
+    q.z = a->conf_logits;
+    q.temp = a->temperature;
+    q.reset = a->reset;
+    q.now_out = a->conf_now;
+    q.out = a->conf_out;
+    q.status_out = a->device_status;
+    hipLaunchKernelGGL(sv_conf_kernel, dim3(a->B), dim3(kThreads), 0, s, q, h->aux);
+    hipLaunchKernelGGL(sv_conf_status_kernel, dim3(1), dim3(64), 0, s, q, h->aux);
+    return hipGetLastError() == hipSuccess ? SV_OK : SV_EDEVICE;
+}
+
 int spec_verify_sched_check(const spec_verify_config* cfg, const spec_verify_sched_args* a)
 {
     int rc = check_config(cfg);
@@ -1618,9 +1787,9 @@ int spec_verify_schedule(spec_verify_t* h, const spec_verify_sched_args* a, void
     q.expected = a->expected_rate;
     q.status_out = a->device_status;
     const unsigned N = (unsigned)(a->B * a->K);
-    hipLaunchKernelGGL(sv_sched_surv_kernel, dim3((a->B + kThreads - 1) / kThreads), dim3(kThreads), 0, s, q, h->w);
-    hipLaunchKernelGGL(sv_sched_rank_kernel, dim3(N), dim3(kThreads), 0, s, q, h->w);
-    hipLaunchKernelGGL(sv_sched_pick_kernel, dim3(1), dim3(kSchedThreads), 0, s, q, h->w);
+    hipLaunchKernelGGL(sv_sched_surv_kernel, dim3((a->B + kThreads - 1) / kThreads), dim3(kThreads), 0, s, q, h->aux);
+    hipLaunchKernelGGL(sv_sched_rank_kernel, dim3(N), dim3(kThreads), 0, s, q, h->aux);
+    hipLaunchKernelGGL(sv_sched_pick_kernel, dim3(1), dim3(kSchedThreads), 0, s, q, h->aux);
     return hipGetLastError() == hipSuccess ? SV_OK : SV_EDEVICE;
 }
 
@@ -1694,65 +1863,21 @@ int spec_verify_run(spec_verify_t* h, const spec_verify_args* a, void* hip_strea
         }
     };
     const int bf = h->cfg.dtype == SV_BF16;
-    const unsigned B = (unsigned)p.B;
-
-    mark(K_PLAN, 0);
-    hipLaunchKernelGGL(sv_plan_kernel, dim3((B + kThreads - 1) / kThreads), dim3(kThreads), 0, s, p, h->w);
-    mark(K_PLAN, 1);
-
-    // groups of positions along the block: 2, 2, 4, 8, ... (a remainder of one
-    // position joins the previous group)
-    int j0 = 1, gsz = 2;
-    const int npos = p.K + 1;
-    while (j0 <= npos) {
-        int G = gsz;
-        if (npos - (j0 + G - 1) <= 1) G = npos - j0 + 1;
-        if (G > kMaxGroup) G = kMaxGroup;
-        const unsigned grid = (unsigned)((long long)B * ((greedy || p.onehot) ? G : 2 * G) * p.nsplit);
-        mark(K_ROWS, 0);
-        if (bf) {
-            if (vec) { if (greedy) launch_rows<SV_BF16, true, true>(grid, s, p, h->w, j0, G); else launch_rows<SV_BF16, true, false>(grid, s, p, h->w, j0, G); }
-            else { if (greedy) launch_rows<SV_BF16, false, true>(grid, s, p, h->w, j0, G); else launch_rows<SV_BF16, false, false>(grid, s, p, h->w, j0, G); }
-        } else {
-            if (vec) { if (greedy) launch_rows<SV_F32, true, true>(grid, s, p, h->w, j0, G); else launch_rows<SV_F32, true, false>(grid, s, p, h->w, j0, G); }
-            else { if (greedy) launch_rows<SV_F32, false, true>(grid, s, p, h->w, j0, G); else launch_rows<SV_F32, false, false>(grid, s, p, h->w, j0, G); }
-        }
-        mark(K_ROWS, 1);
-        mark(K_DECIDE, 0);
-        if (bf) {
-            if (greedy) hipLaunchKernelGGL((sv_decide_kernel<SV_BF16, true>), dim3(B), dim3(kThreads), 0, s, p, h->w, j0, G);
-            else hipLaunchKernelGGL((sv_decide_kernel<SV_BF16, false>), dim3(B), dim3(kThreads), 0, s, p, h->w, j0, G);
-        } else {
-            if (greedy) hipLaunchKernelGGL((sv_decide_kernel<SV_F32, true>), dim3(B), dim3(kThreads), 0, s, p, h->w, j0, G);
-            else hipLaunchKernelGGL((sv_decide_kernel<SV_F32, false>), dim3(B), dim3(kThreads), 0, s, p, h->w, j0, G);
-        }
-        mark(K_DECIDE, 1);
-        j0 += G;
-        gsz = gsz < kMaxGroup ? (j0 <= 3 ? 2 : gsz * 2) : kMaxGroup;
-    }
-
-    mark(K_RESID, 0);
-    if (!greedy) {
-        const dim3 g(B * (unsigned)p.nsplit);
-        if (bf) {
-            if (vec) hipLaunchKernelGGL((sv_resid_kernel<SV_BF16, true>), g, dim3(kThreads), 0, s, p, h->w);
-            else hipLaunchKernelGGL((sv_resid_kernel<SV_BF16, false>), g, dim3(kThreads), 0, s, p, h->w);
-        } else {
-            if (vec) hipLaunchKernelGGL((sv_resid_kernel<SV_F32, true>), g, dim3(kThreads), 0, s, p, h->w);
-            else hipLaunchKernelGGL((sv_resid_kernel<SV_F32, false>), g, dim3(kThreads), 0, s, p, h->w);
-        }
-    }
-    mark(K_RESID, 1);
-
-    mark(K_DRAW, 0);
+    const int mode = (p.onehot ? MODE_ONEHOT : 0) | (p.toff ? MODE_PACKED : 0);
+    // runtime choices -> kernel variants (greedy steps never take the one-hot variant)
+#define SV_STEP(DT, VEC, GR, M) enqueue_step<DT, VEC, GR, M>(h, p, s, mark)
+#define SV_STEP_M(DT, VEC, GR) do { switch (GR ? (mode & MODE_PACKED) : mode) { \
+        case 0: SV_STEP(DT, VEC, GR, 0); break; case 1: SV_STEP(DT, VEC, GR, 1); break; \
+        case 2: SV_STEP(DT, VEC, GR, 2); break; default: SV_STEP(DT, VEC, GR, 3); break; } } while (0)
     if (bf) {
-        if (vec) hipLaunchKernelGGL((sv_draw_kernel<SV_BF16, true>), dim3(B), dim3(kThreads), 0, s, p, h->w);
-        else hipLaunchKernelGGL((sv_draw_kernel<SV_BF16, false>), dim3(B), dim3(kThreads), 0, s, p, h->w);
+        if (vec) { if (greedy) SV_STEP_M(SV_BF16, true, true); else SV_STEP_M(SV_BF16, true, false); }
+        else { if (greedy) SV_STEP_M(SV_BF16, false, true); else SV_STEP_M(SV_BF16, false, false); }
     } else {
-        if (vec) hipLaunchKernelGGL((sv_draw_kernel<SV_F32, true>), dim3(B), dim3(kThreads), 0, s, p, h->w);
-        else hipLaunchKernelGGL((sv_draw_kernel<SV_F32, false>), dim3(B), dim3(kThreads), 0, s, p, h->w);
+        if (vec) { if (greedy) SV_STEP_M(SV_F32, true, true); else SV_STEP_M(SV_F32, true, false); }
+        else { if (greedy) SV_STEP_M(SV_F32, false, true); else SV_STEP_M(SV_F32, false, false); }
     }
-    mark(K_DRAW, 1);
+#undef SV_STEP_M
+#undef SV_STEP
     if (timing) h->timing_n++;
 
     return hipGetLastError() == hipSuccess ? SV_OK : SV_EDEVICE;

@@ -238,6 +238,50 @@ typedef struct {
     int32_t* device_status;       /* optional [1] */
 } spec_verify_sched_args;
 
+/*
+ * Calibrated, causally delayed confidences (the input of the two calls above).
+ *
+ *   umans.ai blog, section "2. Verify smarter": raw confidence is calibrated
+ *   with a per-position temperature fitted on held-out data, and the
+ *   production version sizes the truncation from confidence measured two
+ *   steps earlier, a causal barrier between the decision and the tokens it
+ *   could otherwise peek at.  zhichai.net article, section "Under the hood":
+ *   Sequential Temperature Scaling.
+ *
+ * Each call takes this step's raw confidence logits z [B][K] (slot b, drafted
+ * position j) and per-position temperatures T [K]:
+ *   conf_now[b][j] = sigmoid(z_bj / T_j)   (fp64, rounded to fp32; a temperature
+ *                    that is not finite and positive gives 0 and raises
+ *                    SV_STATUS_BAD_INPUT),
+ *   conf_out[b][j] = the conf_now of slot b, position j from `delay` calls
+ *                    earlier, or c_default while the slot has recorded fewer
+ *                    than `delay` calls since its last reset (delay 0: conf_now).
+ * The handle keeps the last SV_MAX_CONF_DELAY calls of every slot (zero from
+ * create on).  reset[b] != 0 says slot b holds a new sequence from this call on:
+ * its history is dropped first.  Keep K fixed while a slot's history is in use.
+ * conf_out feeds spec_verify_schedule (confidence) or spec_verify_run (tau mode).
+ * Fitting the temperatures is not part of the library.
+ * Limits: B <= max_batch, K <= max_draft, max_batch * max_draft <=
+ * SV_MAX_SCHED_CANDIDATES (the history is sized at create).  Host checks as for
+ * the other calls; calls on one handle must not overlap.
+ */
+#define SV_MAX_CONF_DELAY 4
+
+typedef struct {
+    int32_t B, K;
+    const float* conf_logits;     /* device [B][K] */
+    const float* temperature;     /* device [K] */
+    const int32_t* reset;         /* optional device [B] */
+    int32_t delay;                /* 0 .. SV_MAX_CONF_DELAY */
+    float c_default;
+    float* conf_now;              /* optional device [B][K] */
+    float* conf_out;              /* device [B][K] */
+    int32_t* device_status;       /* optional device [1] */
+} spec_verify_conf_args;
+
+int spec_verify_conf_check(const spec_verify_config* cfg, const spec_verify_conf_args* a);
+int spec_verify_confidence(spec_verify_t* h, const spec_verify_conf_args* a, void* hip_stream);
+
 /* Host-only check of a spec_verify_schedule call.  Returns SV_OK, SV_EINVAL or
  * SV_EUNSUPPORTED. */
 int spec_verify_sched_check(const spec_verify_config* cfg, const spec_verify_sched_args* a);

@@ -162,3 +162,18 @@ def test_sched_check_limits(B):
     assert B.sched_check(cfg, a) == B.SV_EUNSUPPORTED   # 131072 candidates
     a = B.make_sched_args(1024, 64, confidence=fake, speed=fake, n_speed=10 ** 6, verify_len_out=fake)
     assert B.sched_check(cfg, a) == B.SV_OK
+
+
+def test_conf_check(B):
+    cfg = B.Config(8, 8, 1000, B.SV_BF16, 0)
+    fake = 1 << 40
+    a = B.make_conf_args(3, 4, conf_logits=fake, temperature=fake, conf_out=fake)
+    assert B.conf_check(cfg, a) == B.SV_OK
+    for field, value in (("B", 9), ("K", 0), ("K", 9), ("delay", -1), ("delay", 5), ("conf_logits", None),
+                         ("temperature", None), ("conf_out", None)):
+        a = B.make_conf_args(3, 4, conf_logits=fake, temperature=fake, conf_out=fake)
+        setattr(a, field, value)
+        assert B.conf_check(cfg, a) == B.SV_EINVAL, field
+    big = B.Config(70000, 2, 1000, B.SV_BF16, 0)
+    a = B.make_conf_args(3, 2, conf_logits=fake, temperature=fake, conf_out=fake)
+    assert B.conf_check(big, a) == B.SV_EUNSUPPORTED
