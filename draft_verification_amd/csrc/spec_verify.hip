@@ -68,6 +68,7 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kSplit = 16384;                     // elements per split (fixed for batch invariance)
 constexpr int kPerLane = kSplit / kThreads;       // 64 elements per lane per split
 constexpr int kMaxGroup = 16;                     // positions per group
+constexpr int kMaxGroups = 64;                    // groups per step (K + 1 <= 2 + 2 + 4 + 8 + 16 * 59)
 
 enum { CTL_STATUS = 0, CTL_SCHED_STATUS = 1, CTL_CONF_STATUS = 2, CTL_WORDS = 64 };
 enum { FL_ACC = 1, FL_LEN = 2 };
@@ -721,12 +722,47 @@ __global__ __launch_bounds__(kThreads) void sv_decide_kernel(Params p, Work w, i
     __shared__ int sG[kMaxGroup];
     __shared__ double sRatio[kMaxGroup];
     __shared__ float sLseT[kMaxGroup], sLseD[kMaxGroup];
+    __shared__ int sTok[kMaxGroup];
+    __shared__ float sU[kMaxGroup];
     const int b = blockIdx.x, tid = threadIdx.x, K = p.K;
-    const int flags0 = w.st[b].flags, L0 = w.st[b].L;
-    if (!(flags0 & (FL_ACC | FL_LEN))) return;
     const int n = min(j0 + G - 1, K + 1) - j0 + 1;
     const int sw = p.seg_w;
     const int per = 2 * n * sw;
+    // Everything the group's decisions read is requested at once: the state,
+    // the split partials of every row of the group, the drafted tokens' logits,
+    // tokens and uniforms.  Their addresses depend on the group only (rows that
+    // were not streamed are loaded too and masked below), so one round trip
+    // serves them all.
+    const SeqState st0 = w.st[b];
+    float pm = -INFINITY, pd = 0.0f;
+    double ps = 0.0;
+    int pix = 0x7fffffff;
+    if (tid < per && per <= kThreads) {
+        const int pk = tid / sw, k = tid % sw, q = pk >> 1, kind = pk & 1, j = j0 + q;
+        if (k < p.nsplit && (kind == 0 || (!GREEDY && !OH && j <= K))) {
+            const long long pi = part_index(p, b, kind ? K + j : j - 1) + k;
+            pm = w.part_m[pi];
+            if (GREEDY) {
+                pix = w.part_i[pi];
+            } else {
+                ps = w.part_s[pi];
+                pd = w.part_d[pi];
+            }
+        }
+    }
+    float xl = 0.0f;
+    {
+        const int q = tid & 63, kind = tid >> 6, j = j0 + q;
+        if (!GREEDY && kind < 2 && q < n && j <= K && !(kind && OH))
+            xl = w.xlog[(long long)b * (2 * K + 1) + (kind ? K + j : j - 1)];
+        if (kind == 2 && q < n && j <= K) {
+            sTok[q] = p.tok[(long long)b * K + (j - 1)];
+            if (!GREEDY) sU[q] = p.u[(long long)b * (K + 1) + (j - 1)];
+        }
+    }
+    const float tau_b = (!GREEDY && p.derived) ? p.tau[b] : 0.0f;
+    const int flags0 = st0.flags, L0 = st0.L;
+    if (!(flags0 & (FL_ACC | FL_LEN))) return;
     for (int base = 0; base < per; base += kThreads) {
         const int t = base + tid;
         const int pk = t / sw, k = t % sw;
@@ -734,18 +770,25 @@ __global__ __launch_bounds__(kThreads) void sv_decide_kernel(Params p, Work w, i
         const bool read = t < per && (kind ? (!GREEDY && !OH && draft_row_needed(flags0, L0, j, K))
                                            : target_row_needed(flags0, L0, j, K));
         const bool has = read && k < p.nsplit;
-        const long long pi = has ? part_index(p, b, kind ? K + j : j - 1) + k : 0;
+        if (per > kThreads) {
+            // groups wider than one workgroup's threads (very large vocabularies)
+            const long long pi = has ? part_index(p, b, kind ? K + j : j - 1) + k : 0;
+            pm = has ? w.part_m[pi] : -INFINITY;
+            if (GREEDY) pix = has ? w.part_i[pi] : 0x7fffffff;
+            else {
+                ps = has ? w.part_s[pi] : 0.0;
+                pd = has ? w.part_d[pi] : 0.0f;
+            }
+        }
         if (GREEDY) {
-            float v = has ? w.part_m[pi] : -INFINITY;
-            int ix = has ? w.part_i[pi] : 0x7fffffff;
+            float v = has ? pm : -INFINITY;
+            int ix = has ? pix : 0x7fffffff;
             seg_argmax(v, ix, sw);
             if (read && k == 0) { sMt[q] = v; sG[q] = ix; }
         } else {
-            const float m = has ? w.part_m[pi] : -INFINITY;
-            const double sv = has ? w.part_s[pi] : 0.0;
-            const float dv = has ? w.part_d[pi] : 0.0f;
+            const float m = has ? pm : -INFINITY;
             const float M = seg_max(m, sw);
-            double v = (has && m != -INFINITY) ? sv * exp2_f64(((double)m - (double)M) * p.c64 - (double)dv) : 0.0;
+            double v = (has && m != -INFINITY) ? ps * exp2_f64(((double)m - (double)M) * p.c64 - (double)pd) : 0.0;
             v = seg_sum(v, sw);
             if (read && k == 0) {
                 if (kind) { sMd[q] = M; sSd[q] = v; }
@@ -764,10 +807,10 @@ __global__ __launch_bounds__(kThreads) void sv_decide_kernel(Params p, Work w, i
                     sLd[q] = 0.0f;
                     sMd[q] = 0.0f;
                     sSd[q] = 1.0;
+                } else if (kind) {
+                    sLd[q] = xl;
                 } else {
-                    const float v = w.xlog[(long long)b * (2 * K + 1) + (kind ? K + j : j - 1)];
-                    if (kind) sLd[q] = v;
-                    else sLt[q] = v;
+                    sLt[q] = xl;
                 }
             }
         }
@@ -796,7 +839,7 @@ __global__ __launch_bounds__(kThreads) void sv_decide_kernel(Params p, Work w, i
     __syncthreads();
     if (tid != 0) return;
 
-    SeqState st = w.st[b];
+    SeqState st = st0;
     bool acc = (flags0 & FL_ACC) != 0;
     bool len = (flags0 & FL_LEN) != 0;
     for (int q = 0; q < n; ++q) {
@@ -813,7 +856,7 @@ __global__ __launch_bounds__(kThreads) void sv_decide_kernel(Params p, Work w, i
                 st.S = S;
                 if (p.surv) p.surv[(long long)b * K + (j - 1)] = (float)S;
                 if (len) {
-                    if (S >= (double)p.tau[b]) {
+                    if (S >= (double)tau_b) {
                         if (j == K) { st.L = K; len = false; }
                     } else {
                         st.L = j - 1;
@@ -825,7 +868,7 @@ __global__ __launch_bounds__(kThreads) void sv_decide_kernel(Params p, Work w, i
         if (!acc) continue;
         const bool verify = len || st.L >= j; // open length walk means S_j >= tau, so L >= j
         if (verify) {
-            const int x = p.tok[(long long)b * K + (j - 1)];
+            const int x = sTok[q];
             if (x < 0 || x >= p.V) {
                 st.kind = KIND_BAD;
                 st.a = 0;
@@ -841,7 +884,7 @@ __global__ __launch_bounds__(kThreads) void sv_decide_kernel(Params p, Work w, i
                 }
             } else {
                 const double ratio = sRatio[q];
-                const double uj = (double)p.u[(long long)b * (K + 1) + (j - 1)];
+                const double uj = (double)sU[q];
                 if (uj < ratio) {
                     st.a = j;
                 } else {
@@ -923,7 +966,7 @@ __device__ __forceinline__ double draw_mass(float lt, float ld, const DrawCtx& c
     const float pf = scaled_exp2(lt, c.Mt, c.c_hi, c.c_lo) * c.invSt;
     const float qf = resid ? scaled_exp2(ld, c.Md, c.c_hi, c.c_lo) * c.invSd : 0.0f;
     if (fmaxf(pf, qf) > 0x1p-9f) return mass_f64(lt, ld, c, resid);
-    return pf > qf ? (double)(pf - qf) : 0.0;
+    return (double)fmaxf(pf - qf, 0.0f);
 }
 
 // Inclusive prefix sum over the 64 lanes of a wavefront (fixed order).
@@ -945,16 +988,18 @@ template <int RUN>
 __device__ __forceinline__ double run_mass(const float (&lt)[RUN], const float (&ld)[RUN], const DrawCtx& c, bool resid,
                                            bool& slow)
 {
+    // fmaxf(pf - qf, 0) equals (pf > qf ? pf - qf : 0) for these finite
+    // values; the run is tested once, on its largest p or q
     double acc = 0.0;
-    bool big = false;
+    float big = 0.0f;
 #pragma unroll
     for (int i = 0; i < RUN; ++i) {
         const float pf = scaled_exp2(lt[i], c.Mt, c.c_hi, c.c_lo) * c.invSt;
         const float qf = resid ? scaled_exp2(ld[i], c.Md, c.c_hi, c.c_lo) * c.invSd : 0.0f;
-        big |= fmaxf(pf, qf) > 0x1p-9f;
-        acc += (double)(pf > qf ? pf - qf : 0.0f);
+        big = fmaxf(big, fmaxf(pf, qf));
+        acc += (double)fmaxf(pf - qf, 0.0f);
     }
-    slow = big;
+    slow = big > 0x1p-9f;
     return acc;
 }
 
@@ -1150,7 +1195,7 @@ __global__ __launch_bounds__(kThreads) void sv_draw_kernel(Params p, Work w)
                 } else {
                     const float pf = scaled_exp2(lt[i], c.Mt, c.c_hi, c.c_lo) * c.invSt;
                     const float qf = resid ? scaled_exp2(ld[i], c.Md, c.c_hi, c.c_lo) * c.invSd : 0.0f;
-                    m[i] = (double)(pf > qf ? pf - qf : 0.0f);
+                    m[i] = (double)fmaxf(pf - qf, 0.0f);
                 }
                 if (m[i] > 0.0) lastpos = i0 + i;
             }
@@ -1443,25 +1488,30 @@ void enqueue_step(const spec_verify* h, const Params& p, hipStream_t s, Mark& ma
 {
     constexpr bool OH = (MODE & MODE_ONEHOT) != 0;
     const unsigned B = (unsigned)p.B;
-    mark(K_PLAN, 0);
-    hipLaunchKernelGGL(sv_plan_kernel, dim3((B + kThreads - 1) / kThreads), dim3(kThreads), 0, s, p, h->w);
-    mark(K_PLAN, 1);
-    int j0 = 1, gsz = 2;
+    int gj[kMaxGroups], gn[kMaxGroups], ng = 0;
     const int npos = p.K + 1;
-    while (j0 <= npos) {
+    for (int j0 = 1, gsz = 2; j0 <= npos; ++ng) {
         int G = gsz;
         if (npos - (j0 + G - 1) <= 1) G = npos - j0 + 1;
         if (G > kMaxGroup) G = kMaxGroup;
-        const unsigned grid = (unsigned)((long long)B * ((GR || OH) ? G : 2 * G) * p.nsplit);
-        mark(K_ROWS, 0);
-        hipLaunchKernelGGL((sv_rows_kernel<DT, VEC, GR, MODE>), dim3(grid), dim3(kThreads), 0, s, p, h->w, j0, G);
-        mark(K_ROWS, 1);
-        mark(K_DECIDE, 0);
-        hipLaunchKernelGGL((sv_decide_kernel<DT, GR, MODE & MODE_ONEHOT>), dim3(B), dim3(kThreads), 0, s, p, h->w, j0,
-                           G);
-        mark(K_DECIDE, 1);
+        gj[ng] = j0;
+        gn[ng] = G;
         j0 += G;
         gsz = gsz < kMaxGroup ? (j0 <= 3 ? 2 : gsz * 2) : kMaxGroup;
+    }
+    auto slots = [&](int g) { return (GR || OH) ? gn[g] : 2 * gn[g]; };
+    mark(K_PLAN, 0);
+    hipLaunchKernelGGL(sv_plan_kernel, dim3((B + kThreads - 1) / kThreads), dim3(kThreads), 0, s, p, h->w);
+    mark(K_PLAN, 1);
+    for (int g = 0; g < ng; ++g) {
+        const unsigned grid = (unsigned)((long long)B * slots(g) * p.nsplit);
+        mark(K_ROWS, 0);
+        hipLaunchKernelGGL((sv_rows_kernel<DT, VEC, GR, MODE>), dim3(grid), dim3(kThreads), 0, s, p, h->w, gj[g], gn[g]);
+        mark(K_ROWS, 1);
+        mark(K_DECIDE, 0);
+        hipLaunchKernelGGL((sv_decide_kernel<DT, GR, MODE & MODE_ONEHOT>), dim3(B), dim3(kThreads), 0, s, p, h->w,
+                           gj[g], gn[g]);
+        mark(K_DECIDE, 1);
     }
     mark(K_RESID, 0);
     if (!GR)
