@@ -101,7 +101,6 @@ struct Work {
     int* part_i;      // same layout, split argmax (greedy)
     SeqState* st;     // [max_batch]
     int* live;        // [max_batch] (L + 1) << 2 | flags, the part of st that sv_rows reads
-    double* rsum;     // [max_batch][nsplit] residual mass per split
     double* seg;      // [max_batch][nsplit][64] residual mass per segment of a split
     float* xlog;      // [max_batch][2K+1] logit of the drafted token in each row
 };
@@ -369,6 +368,97 @@ struct Chunk<SV_F32> {
 #pragma unroll
         for (int k = 0; k < 16; ++k)
             if (base + k * 1024 + lane * 4 >= V) w[4 * k] = w[4 * k + 1] = w[4 * k + 2] = w[4 * k + 3] = -INFINITY;
+    }
+};
+
+// A quarter of a split (kParts parts): loads q NL .. q NL + NL - 1 of the
+// split layout above, 16 elements per lane.  Element e of the part is element
+// q PER + e of the lane's split elements.
+constexpr int kParts = 4;
+
+template <int DT>
+struct Part;
+
+template <>
+struct Part<SV_BF16> {
+    static constexpr int NL = 8 / kParts, PER = 8 * NL;
+    uint32_t w[PER / 2];
+    __device__ __forceinline__ float get(int e) const { return (e & 1) ? bf16_hi(w[e >> 1]) : bf16_lo(w[e >> 1]); }
+    // element of this lane's part holding split offset off, or -1
+    __device__ __forceinline__ static int owned(int off, int q, int lane)
+    {
+        const int k = off >> 11;
+        return ((off >> 3) & 255) == lane && k / NL == q ? (k % NL) * 8 + (off & 7) : -1;
+    }
+    __device__ __forceinline__ void one_hot(int e)
+    {
+#pragma unroll
+        for (int k = 0; k < PER / 2; ++k) {
+            const uint32_t lo = 2 * k == e ? 0x0000u : 0xFF80u, hi = 2 * k + 1 == e ? 0x0000u : 0xFF80u;
+            w[k] = lo | (hi << 16);
+        }
+    }
+    template <bool VEC>
+    __device__ __forceinline__ void load(const void* row, int base, int V, int lane, int q)
+    {
+        const uint16_t* r = (const uint16_t*)row;
+#pragma unroll
+        for (int k = 0; k < NL; ++k) {
+            const int i0 = base + (q * NL + k) * 2048 + lane * 8;
+            if (VEC) {
+                if (i0 < V) {
+                    const uint4 v = *(const uint4*)(r + i0);
+                    w[4 * k] = v.x; w[4 * k + 1] = v.y; w[4 * k + 2] = v.z; w[4 * k + 3] = v.w;
+                } else {
+                    w[4 * k] = w[4 * k + 1] = w[4 * k + 2] = w[4 * k + 3] = 0xFF80FF80u;
+                }
+            } else {
+#pragma unroll
+                for (int h = 0; h < 4; ++h) {
+                    const int i = i0 + 2 * h;
+                    const uint32_t lo = i < V ? (uint32_t)r[i] : 0xFF80u;
+                    const uint32_t hi = i + 1 < V ? (uint32_t)r[i + 1] : 0xFF80u;
+                    w[4 * k + h] = lo | (hi << 16);
+                }
+            }
+        }
+    }
+};
+
+template <>
+struct Part<SV_F32> {
+    static constexpr int NL = 16 / kParts, PER = 4 * NL;
+    float w[PER];
+    __device__ __forceinline__ float get(int e) const { return w[e]; }
+    __device__ __forceinline__ static int owned(int off, int q, int lane)
+    {
+        const int k = off >> 10;
+        return ((off >> 2) & 255) == lane && k / NL == q ? (k % NL) * 4 + (off & 3) : -1;
+    }
+    __device__ __forceinline__ void one_hot(int e)
+    {
+#pragma unroll
+        for (int k = 0; k < PER; ++k) w[k] = k == e ? 0.0f : -INFINITY;
+    }
+    template <bool VEC>
+    __device__ __forceinline__ void load(const void* row, int base, int V, int lane, int q)
+    {
+        const float* r = (const float*)row;
+#pragma unroll
+        for (int k = 0; k < NL; ++k) {
+            const int i0 = base + (q * NL + k) * 1024 + lane * 4;
+            if (VEC) {
+                if (i0 < V) {
+                    const float4 v = *(const float4*)(r + i0);
+                    w[4 * k] = v.x; w[4 * k + 1] = v.y; w[4 * k + 2] = v.z; w[4 * k + 3] = v.w;
+                } else {
+                    w[4 * k] = w[4 * k + 1] = w[4 * k + 2] = w[4 * k + 3] = -INFINITY;
+                }
+            } else {
+#pragma unroll
+                for (int h = 0; h < 4; ++h) w[4 * k + h] = (i0 + h < V) ? r[i0 + h] : -INFINITY;
+            }
+        }
     }
 };
 
@@ -1037,43 +1127,51 @@ __device__ __forceinline__ void split_segments(const Chunk<DT>& tc, const Chunk<
     }
 }
 
+// One workgroup per (sequence, split, quarter of the split): the residual mass
+// of each of the quarter's segments (w.seg).  Quarters keep the workgroups
+// short and light on registers; the pass is compute-bound (two exponentials
+// per token).
 template <int DT, bool VEC, int MODE>
 __global__ __launch_bounds__(kThreads) void sv_resid_kernel(Params p, Work w)
 {
     constexpr bool OH = (MODE & MODE_ONEHOT) != 0, PK = (MODE & MODE_PACKED) != 0;
     using S = Seg<DT>;
-    __shared__ double s_seg[S::SEGS];
-    const int b = (int)(blockIdx.x / p.nsplit);
-    const int split = (int)(blockIdx.x % p.nsplit);
+    constexpr int NL = Part<DT>::NL, QSEG = NL * kWaves;
+    __shared__ double s_seg[QSEG];
+    const int q = (int)(blockIdx.x % kParts);
+    const int split = (int)((blockIdx.x / kParts) % p.nsplit);
+    const int b = (int)(blockIdx.x / kParts / p.nsplit);
     if (w.st[b].kind != KIND_RESID) return;
     const SeqState st = w.st[b];
     const DrawCtx c = make_ctx(st, p);
-    Chunk<DT> tc, dc;
-    tc.template load<VEC>(seq_row<DT, PK>(p.t, p.toff, p.tbs, p.trs, b, st.js - 1), split * kSplit, p.V, threadIdx.x);
+    const int t = (int)threadIdx.x, lane = t & 63, wv = t >> 6;
+    Part<DT> tc, dc;
+    tc.template load<VEC>(seq_row<DT, PK>(p.t, p.toff, p.tbs, p.trs, b, st.js - 1), split * kSplit, p.V, t, q);
     if (OH) {
         // the one-hot draft row, built in registers: logit 0 at the drafted
-        // token (held by one lane of one split), -inf elsewhere
+        // token (held by one lane of one quarter of one split), -inf elsewhere
         const int x = p.tok[(long long)b * p.K + (st.js - 1)];
         const int off = x - split * kSplit;
-        int e = -1;
-        if (off >= 0 && off < kSplit) {
-            int ol, oe;
-            Chunk<DT>::owner(off, ol, oe);
-            if ((int)threadIdx.x == ol) e = oe;
-        }
-        dc.one_hot(e);
+        dc.one_hot(off >= 0 && off < kSplit ? Part<DT>::owned(off, q, t) : -1);
     } else {
-        dc.template load<VEC>(seq_row<DT, PK>(p.d, p.doff, p.dbs, p.drs, b, st.js - 1), split * kSplit, p.V, threadIdx.x);
+        dc.template load<VEC>(seq_row<DT, PK>(p.d, p.doff, p.dbs, p.drs, b, st.js - 1), split * kSplit, p.V, t, q);
     }
-    split_segments<DT>(tc, dc, c, true, s_seg);
+#pragma unroll
+    for (int k = 0; k < NL; ++k) {
+        float lt[S::RUN], ld[S::RUN];
+#pragma unroll
+        for (int i = 0; i < S::RUN; ++i) {
+            lt[i] = tc.get(k * S::RUN + i);
+            ld[i] = dc.get(k * S::RUN + i);
+        }
+        bool slow;
+        double r = run_mass<S::RUN>(lt, ld, c, true, slow);
+        if (slow) r = run_mass_exact<S::RUN>(lt, ld, c, true); // rare: a large p or q in the run
+        const double incl = wave_incl_scan(r, lane);
+        if (lane == 63) s_seg[k * kWaves + wv] = incl;
+    }
     __syncthreads();
-    const long long so = ((long long)b * p.nsplit + split) * kSegStride;
-    if (threadIdx.x < S::SEGS) w.seg[so + threadIdx.x] = s_seg[threadIdx.x];
-    if (threadIdx.x == 0) {
-        double tot = 0.0;
-        for (int g = 0; g < S::SEGS; ++g) tot += s_seg[g];
-        w.rsum[(long long)b * p.nsplit + split] = tot;
-    }
+    if (t < QSEG) w.seg[((long long)b * p.nsplit + split) * kSegStride + q * QSEG + t] = s_seg[t];
 }
 
 // First lane whose inclusive prefix exceeds w (lanes < n), as (lane, w minus
@@ -1119,7 +1217,13 @@ __global__ __launch_bounds__(kThreads) void sv_draw_kernel(Params p, Work w)
         // 1. the split holding the draw point (wave 0, lane k = split k)
         if (tid < 64) {
             bool resid = kind == KIND_RESID;
-            double m = (resid && lane < p.nsplit) ? w.rsum[(long long)b * p.nsplit + lane] : 0.0;
+            double m = 0.0;
+            if (resid && lane < p.nsplit) {
+                // residual mass of split `lane`: its segments summed in order
+                const double* sg = w.seg + ((long long)b * p.nsplit + lane) * kSegStride;
+#pragma unroll 8
+                for (int g = 0; g < S::SEGS; ++g) m += sg[g];
+            }
             const double Z = __shfl(wave_incl_scan(m, lane), p.nsplit - 1);
             if (resid && !(Z > 0.0)) resid = false; // cannot happen in exact arithmetic after a rejection
             if (!resid) {
@@ -1515,8 +1619,8 @@ void enqueue_step(const spec_verify* h, const Params& p, hipStream_t s, Mark& ma
     }
     mark(K_RESID, 0);
     if (!GR)
-        hipLaunchKernelGGL((sv_resid_kernel<DT, VEC, MODE>), dim3(B * (unsigned)p.nsplit), dim3(kThreads), 0, s, p,
-                           h->w);
+        hipLaunchKernelGGL((sv_resid_kernel<DT, VEC, MODE>), dim3(B * (unsigned)p.nsplit * kParts), dim3(kThreads), 0,
+                           s, p, h->w);
     mark(K_RESID, 1);
     mark(K_DRAW, 0);
     hipLaunchKernelGGL((sv_draw_kernel<DT, VEC, MODE>), dim3(B), dim3(kThreads), 0, s, p, h->w);
@@ -1649,7 +1753,6 @@ int spec_verify_create(const spec_verify_config* cfg, spec_verify_t** out)
     const size_t o_pd = off; off = align_up(off + nrow * ns * sizeof(float));
     const size_t o_st = off; off = align_up(off + (size_t)cfg->max_batch * sizeof(SeqState));
     const size_t o_lv = off; off = align_up(off + (size_t)cfg->max_batch * sizeof(int));
-    const size_t o_rs = off; off = align_up(off + (size_t)cfg->max_batch * ns * sizeof(double));
     const size_t o_sg = off; off = align_up(off + (size_t)cfg->max_batch * ns * kSegStride * sizeof(double));
     const size_t o_xl = off; off = align_up(off + nrow * sizeof(float));
     const long long ncand = std::min((long long)cfg->max_batch * cfg->max_draft, (long long)SV_MAX_SCHED_CANDIDATES);
@@ -1669,7 +1772,6 @@ int spec_verify_create(const spec_verify_config* cfg, spec_verify_t** out)
     h->w.part_i = (int*)(base + o_pi);
     h->w.st = (SeqState*)(base + o_st);
     h->w.live = (int*)(base + o_lv);
-    h->w.rsum = (double*)(base + o_rs);
     h->w.seg = (double*)(base + o_sg);
     h->w.xlog = (float*)(base + o_xl);
     h->aux.ctl = h->w.ctl;
