@@ -774,6 +774,66 @@ __global__ __launch_bounds__(kThreads, (DT == SV_BF16 && VEC) ? 8 : 1) void sv_r
     rows_finish<DT, GREEDY>(p, w, c, r, redf, redd, redi, t);
 }
 
+// The same statistics for the last position group from the fourth group on,
+// where the walks of most sequences have ended (typically one in ten is still
+// open) and one workgroup per row would mostly start only to find its row
+// unneeded.  The group's rows (sequence, row slot) are dealt to nw =
+// gridDim.x / nsplit workgroup columns: column c takes rows c, c + nw, ...,
+// kRowsLate of them.  Lanes 0 .. kRowsLate-1 read those sequences' states at
+// once, and the workgroup streams the needed ones in turn.  Each turn is a
+// separate straight-line copy of the row code (a schedule barrier between
+// copies, the thread index re-derived in each) so that the copies neither
+// share registers nor overlap: registers bound the loads in flight.
+constexpr int kRowsLate = 4;
+
+template <int DT, bool VEC, bool GREEDY, int MODE>
+__global__ __launch_bounds__(kThreads, (DT == SV_BF16 && VEC) ? 8 : 1) void sv_rows_late_kernel(Params p, Work w,
+                                                                                                int j0, int G)
+{
+    constexpr bool OH = (MODE & MODE_ONEHOT) != 0, PK = (MODE & MODE_PACKED) != 0;
+    __shared__ float redf[kWaves];
+    __shared__ double redd[kWaves];
+    __shared__ int redi[kWaves];
+    const int t = (int)threadIdx.x, lane = t & 63;
+    const int split = (int)(blockIdx.x % (unsigned)p.nsplit);
+    const int col = (int)(blockIdx.x / (unsigned)p.nsplit);
+    const int nw = (int)(gridDim.x / (unsigned)p.nsplit);
+    const int slots = (GREEDY || OH) ? G : 2 * G;
+    const int nrow = p.B * slots;
+    bool need = false;
+    if (lane < kRowsLate) {
+        const int i = col + lane * nw;
+        if (i < nrow) {
+            const int b = i / slots, slot = i % slots;
+            const int lv = w.live[b];
+            const int flags = lv & 3, L = (lv >> 2) - 1;
+            const bool draft = !GREEDY && slot >= G;
+            const int j = j0 + (draft ? slot - G : slot);
+            need = draft ? draft_row_needed(flags, L, j, p.K) : target_row_needed(flags, L, j, p.K);
+        }
+    }
+    const unsigned long long mask = __ballot(need); // the same in every wavefront
+    const int wv = __builtin_amdgcn_readfirstlane(t >> 6);
+#pragma unroll
+    for (int k = 0; k < kRowsLate; ++k) {
+        __builtin_amdgcn_sched_barrier(0);
+        if ((mask >> k) & 1) {
+            const int i = col + k * nw;
+            const int b = i / slots, slot = i % slots;
+            const bool draft = !GREEDY && slot >= G;
+            const int j = j0 + (draft ? slot - G : slot);
+            int z = 0;
+            asm volatile("" : "+v"(z)); // opaque: the index below is computed afresh in this copy
+            const int tl = (wv << 6) | (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, (unsigned)z));
+            const RowRef r = row_ref<DT, PK>(p, b, j, draft, split);
+            Chunk<DT> c;
+            c.template issue<VEC>(r.row, split * kSplit, p.V, tl);
+            c.template fix_tail<VEC>(split * kSplit, p.V, tl);
+            rows_finish<DT, GREEDY>(p, w, c, r, redf, redd, redi, tl);
+        }
+    }
+}
+
 // ---------------------------------------------------------------- sv_decide
 //
 // One workgroup per sequence.  Threads take (position, row, split) triples and
@@ -1608,9 +1668,15 @@ void enqueue_step(const spec_verify* h, const Params& p, hipStream_t s, Mark& ma
     hipLaunchKernelGGL(sv_plan_kernel, dim3((B + kThreads - 1) / kThreads), dim3(kThreads), 0, s, p, h->w);
     mark(K_PLAN, 1);
     for (int g = 0; g < ng; ++g) {
-        const unsigned grid = (unsigned)((long long)B * slots(g) * p.nsplit);
+        const long long nrow = (long long)B * slots(g);
         mark(K_ROWS, 0);
-        hipLaunchKernelGGL((sv_rows_kernel<DT, VEC, GR, MODE>), dim3(grid), dim3(kThreads), 0, s, p, h->w, gj[g], gn[g]);
+        if (VEC && g >= 3 && g + 1 == ng) // (the unaligned path keeps one row per workgroup)
+            hipLaunchKernelGGL((sv_rows_late_kernel<DT, true, GR, MODE>),
+                               dim3((unsigned)((nrow + kRowsLate - 1) / kRowsLate * p.nsplit)), dim3(kThreads), 0, s,
+                               p, h->w, gj[g], gn[g]);
+        else
+            hipLaunchKernelGGL((sv_rows_kernel<DT, VEC, GR, MODE>), dim3((unsigned)(nrow * p.nsplit)), dim3(kThreads),
+                               0, s, p, h->w, gj[g], gn[g]);
         mark(K_ROWS, 1);
         mark(K_DECIDE, 0);
         hipLaunchKernelGGL((sv_decide_kernel<DT, GR, MODE & MODE_ONEHOT>), dim3(B), dim3(kThreads), 0, s, p, h->w,
