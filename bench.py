@@ -322,6 +322,18 @@ def main():
     torch.cuda.synchronize()
     ms_step = ev0.elapsed_time(ev1) / args.steps
 
+    # distribution of single steps: an event between consecutive steps (same stream)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    evs[0].record()
+    for i in range(args.steps):
+        sv.run(argv[i % 2], stream)
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    per_step = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)])
+    step_dist = {"p10": float(np.percentile(per_step, 10)), "p50": float(np.median(per_step)),
+                 "p90": float(np.percentile(per_step, 90)), "n": int(args.steps), "unit": "ms",
+                 "method": "HIP events between consecutive steps on the launch stream (a separate pass)"}
+
     # per-kernel timing (HIP events around each launch, same stream)
     sv.timing_begin(args.steps)
     for i in range(args.steps):
@@ -373,6 +385,7 @@ def main():
                      "per_launch_means": "per step: the sv_rows launches of one step (one per position group)",
                      "traffic_source": "rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated, bytes per step; null "
                                        "when the kernel source changed since the counters were taken"},
+        "step_ms_distribution": step_dist,
         "step_hbm_gbps": bytes_step / (ms_step / 1e3) / 1e9,
         "emitted_tokens_per_s": float(np.mean([o["accepted_len"].sum() + w.B for o in outs])) / (ms_step / 1e3),
         "mean_accepted": mean_a,

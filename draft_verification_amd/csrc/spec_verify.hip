@@ -1262,11 +1262,16 @@ __global__ __launch_bounds__(kThreads) void sv_draw_kernel(Params p, Work w)
 {
     constexpr bool OH = (MODE & MODE_ONEHOT) != 0, PK = (MODE & MODE_PACKED) != 0;
     using S = Seg<DT>;
-    __shared__ double s_seg[S::SEGS];
+    extern __shared__ double s_all[];  // [nsplit][SEGS] residual segment sums of the sequence
+    __shared__ double s_bonus[S::SEGS]; // segment sums of the bonus draw's split
     __shared__ double s_wrel, s_Z, s_my;
     __shared__ int s_split, s_resid, s_y;
     const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
     const int K = p.K;
+    // requested together with the state: the final draw's uniform and the
+    // drafted tokens this thread copies to the output
+    const float uf32 = (p.u == nullptr) ? 0.0f : p.u[(long long)b * (K + 1) + K];
+    const int tok0 = tid < K ? p.tok[(long long)b * K + tid] : -1;
     const SeqState st = w.st[b];
     int kind = st.kind;
     int a = st.a;
@@ -1274,15 +1279,22 @@ __global__ __launch_bounds__(kThreads) void sv_draw_kernel(Params p, Work w)
     float zrep = NAN, py = NAN;
 
     if (kind == KIND_RESID || kind == KIND_BONUS) {
+        if (kind == KIND_RESID) {
+            // every segment sum of the sequence at once (one round trip): the
+            // split totals and the search inside the chosen split both read LDS
+            const double* sg = w.seg + (long long)b * p.nsplit * kSegStride;
+            for (int i = tid; i < p.nsplit * S::SEGS; i += kThreads)
+                s_all[i] = sg[(i / S::SEGS) * kSegStride + i % S::SEGS];
+            __syncthreads();
+        }
         // 1. the split holding the draw point (wave 0, lane k = split k)
         if (tid < 64) {
             bool resid = kind == KIND_RESID;
             double m = 0.0;
             if (resid && lane < p.nsplit) {
                 // residual mass of split `lane`: its segments summed in order
-                const double* sg = w.seg + ((long long)b * p.nsplit + lane) * kSegStride;
 #pragma unroll 8
-                for (int g = 0; g < S::SEGS; ++g) m += sg[g];
+                for (int g = 0; g < S::SEGS; ++g) m += s_all[lane * S::SEGS + g];
             }
             const double Z = __shfl(wave_incl_scan(m, lane), p.nsplit - 1);
             if (resid && !(Z > 0.0)) resid = false; // cannot happen in exact arithmetic after a rejection
@@ -1295,7 +1307,7 @@ __global__ __launch_bounds__(kThreads) void sv_draw_kernel(Params p, Work w)
                         m = w.part_s[pb] * exp2_f64(((double)mk - (double)st.Mt) * p.c64 - (double)w.part_d[pb]) / st.St;
                 }
             }
-            const double uf = (double)p.u[(long long)b * (K + 1) + K];
+            const double uf = (double)uf32;
             double wrel;
             int ks = wave_select(m, p.nsplit, resid ? uf * Z : uf, wrel);
             if (ks < 0) { // rounding: the last split with mass, its last token
@@ -1317,16 +1329,15 @@ __global__ __launch_bounds__(kThreads) void sv_draw_kernel(Params p, Work w)
         const void* drow = (resid && !OH) ? seq_row<DT, PK>(p.d, p.doff, p.dbs, p.drs, b, st.js - 1) : nullptr;
         const int xone = (resid && OH) ? p.tok[(long long)b * K + (st.js - 1)] : -1; // one-hot draft token
 
-        // 2. segment sums of that split: stored by sv_resid for a replacement,
-        //    computed here for a bonus draw
-        if (resid) {
-            if (tid < S::SEGS) s_seg[tid] = w.seg[((long long)b * p.nsplit + ks) * kSegStride + tid];
-        } else {
+        // 2. segment sums of that split: stored by sv_resid for a replacement
+        //    (already in LDS), computed here for a bonus draw
+        const double* s_seg = resid ? s_all + ks * S::SEGS : s_bonus;
+        if (!resid) {
             Chunk<DT> tc;
             tc.template load<VEC>(trow, ks * kSplit, p.V, tid);
-            split_segments<DT>(tc, tc, c, false, s_seg);
+            split_segments<DT>(tc, tc, c, false, s_bonus);
+            __syncthreads();
         }
-        __syncthreads();
 
         // 3. segment, lane and token (wave 0)
         if (tid < 64) {
@@ -1379,9 +1390,13 @@ __global__ __launch_bounds__(kThreads) void sv_draw_kernel(Params p, Work w)
                 }
                 if (yy < 0) yy = lastpos >= 0 ? lastpos : i0; // rounding: last token with mass
                 s_y = yy;
-                // the reported probability of the chosen token is evaluated in fp64
-                const float ldy = !resid ? 0.0f : (OH ? (yy == xone ? 0.0f : -INFINITY) : load_one<DT>(drow, yy));
-                s_my = mass_f64(load_one<DT>(trow, yy), ldy, c, resid);
+                // the reported probability of the chosen token is evaluated in
+                // fp64, from the logits this lane holds (yy lies in its run)
+                float lty = lt[0], ldy = ld[0];
+#pragma unroll
+                for (int i = 1; i < S::RUN; ++i)
+                    if (i0 + i == yy) { lty = lt[i]; ldy = ld[i]; }
+                s_my = mass_f64(lty, resid ? ldy : 0.0f, c, resid);
             }
         }
         __syncthreads();
@@ -1398,7 +1413,7 @@ __global__ __launch_bounds__(kThreads) void sv_draw_kernel(Params p, Work w)
 
     for (int jj = tid; jj <= K; jj += kThreads) {
         int v = -1;
-        if (y >= 0) v = jj < a ? p.tok[(long long)b * K + jj] : (jj == a ? y : -1);
+        if (y >= 0) v = jj < a ? (jj == tid ? tok0 : p.tok[(long long)b * K + jj]) : (jj == a ? y : -1);
         p.out_tok[(long long)b * (K + 1) + jj] = v;
     }
     if (tid == 0) {
@@ -1689,7 +1704,8 @@ void enqueue_step(const spec_verify* h, const Params& p, hipStream_t s, Mark& ma
                            s, p, h->w);
     mark(K_RESID, 1);
     mark(K_DRAW, 0);
-    hipLaunchKernelGGL((sv_draw_kernel<DT, VEC, MODE>), dim3(B), dim3(kThreads), 0, s, p, h->w);
+    hipLaunchKernelGGL((sv_draw_kernel<DT, VEC, MODE>), dim3(B), dim3(kThreads),
+                       (size_t)p.nsplit * Seg<DT>::SEGS * sizeof(double), s, p, h->w);
     mark(K_DRAW, 1);
 }
 
