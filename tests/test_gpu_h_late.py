@@ -1,5 +1,5 @@
 """GPU parity of long draft blocks, where the last position group deals several
-rows to each workgroup (four or more position groups: K >= 12).
+rows to each workgroup (four or more position groups: K >= 11).
 
 Acceptance is made high (draft = target + small noise, or a greedy drafter
 that matches often) so that many sequences reach the last group, and low in
@@ -41,17 +41,18 @@ BASE = synth.Workload("late", B=7, K=16, V=16392, dtype=synth.BF16, target_kind=
 
 
 def _last_group_start(K):
-    """First position of the last position group (groups of 2, 2, 4, 8, 16, ...
-    positions over K + 1 rows; a remainder of one joins the group before)."""
-    j0, gsz, start, npos = 1, 2, 1, K + 1
+    """First position of the last position group (groups of 3, 3, 4, 8, 16, 16,
+    ... positions over K + 1 rows; a remainder of one joins the group before)."""
+    first = [3, 3, 4, 8]
+    j0, ng, start, npos = 1, 0, 1, K + 1
     while j0 <= npos:
-        G = gsz
+        G = first[ng] if ng < len(first) else min(first[-1] << (ng - len(first) + 1), 16)
         if npos - (j0 + G - 1) <= 1:
             G = npos - j0 + 1
         G = min(G, 16)
         start = j0
         j0 += G
-        gsz = gsz if gsz >= 16 else (2 if j0 <= 3 else gsz * 2)
+        ng += 1
     return start
 
 
