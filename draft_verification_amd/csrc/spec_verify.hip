@@ -775,16 +775,19 @@ __global__ __launch_bounds__(kThreads, (DT == SV_BF16 && VEC) ? 8 : 1) void sv_r
 }
 
 // The same statistics for the last position group from the fourth group on,
-// where the walks of most sequences have ended (typically one in ten is still
-// open) and one workgroup per row would mostly start only to find its row
-// unneeded.  The group's rows (sequence, row slot) are dealt to nw =
+// where the walks of most sequences have ended (typically a few in a hundred
+// are still open) and one workgroup per row would mostly start only to find
+// its row unneeded.  The group's rows (sequence, row slot) are dealt to nw =
 // gridDim.x / nsplit workgroup columns: column c takes rows c, c + nw, ...,
 // kRowsLate of them.  Lanes 0 .. kRowsLate-1 read those sequences' states at
 // once, and the workgroup streams the needed ones in turn.  Each turn is a
 // separate straight-line copy of the row code (a schedule barrier between
 // copies, the thread index re-derived in each) so that the copies neither
 // share registers nor overlap: registers bound the loads in flight.
-constexpr int kRowsLate = 4;
+// (8 measured best for the last group at 4% of sequences open; 2 or 4 rows per
+// workgroup lost on a group with a quarter of them open, as one row per
+// workgroup then keeps more rows in flight.)
+constexpr int kRowsLate = 8;
 
 template <int DT, bool VEC, bool GREEDY, int MODE>
 __global__ __launch_bounds__(kThreads, (DT == SV_BF16 && VEC) ? 8 : 1) void sv_rows_late_kernel(Params p, Work w,
