@@ -1083,10 +1083,16 @@ struct Seg {
 };
 constexpr int kSegStride = 64; // segment sums stored per split
 
+// The rows' 1/S enter the fp32 masses as two fp32 parts (hi + lo, ~2^-48
+// relative): a single fp32 rounding would scale every p (or q) of the row by the
+// same factor, an error that does not cancel in p - q and is large relative to
+// the residual mass when the rows are nearly equal.
 struct DrawCtx {
-    float Mt, Md, invSt, invSd, c_hi, c_lo;
+    float Mt, Md, iSt_hi, iSt_lo, iSd_hi, iSd_lo, c_hi, c_lo;
     double iSt, iSd, c64;
 };
+
+__device__ __forceinline__ float scale2(float e, float hi, float lo) { return fmaf(e, hi, e * lo); }
 
 __device__ __forceinline__ DrawCtx make_ctx(const SeqState& st, const Params& p)
 {
@@ -1095,8 +1101,10 @@ __device__ __forceinline__ DrawCtx make_ctx(const SeqState& st, const Params& p)
     c.Md = st.Md;
     c.iSt = 1.0 / st.St;
     c.iSd = st.Sd > 0.0 ? 1.0 / st.Sd : 0.0;
-    c.invSt = (float)c.iSt;
-    c.invSd = (float)c.iSd;
+    c.iSt_hi = (float)c.iSt;
+    c.iSt_lo = (float)(c.iSt - (double)c.iSt_hi);
+    c.iSd_hi = (float)c.iSd;
+    c.iSd_lo = (float)(c.iSd - (double)c.iSd_hi);
     c.c_hi = p.c_hi;
     c.c_lo = p.c_lo;
     c.c64 = p.c64;
@@ -1113,11 +1121,11 @@ __device__ __forceinline__ double mass_f64(float lt, float ld, const DrawCtx& c,
 // Mass of one token under the final draw: max(0, p - q) for a replacement,
 // p for a bonus.  fp32 first; masses whose p or q exceeds 2^-9 are evaluated
 // in fp64 (at most 2^10 tokens of a row pair qualify).  Below that, the fp32
-// value carries < 2e-7 relative error, so the CDF error stays below 1e-8.
+// value carries a few 1e-8 relative error, independent from token to token.
 __device__ __forceinline__ double draw_mass(float lt, float ld, const DrawCtx& c, bool resid)
 {
-    const float pf = scaled_exp2(lt, c.Mt, c.c_hi, c.c_lo) * c.invSt;
-    const float qf = resid ? scaled_exp2(ld, c.Md, c.c_hi, c.c_lo) * c.invSd : 0.0f;
+    const float pf = scale2(scaled_exp2(lt, c.Mt, c.c_hi, c.c_lo), c.iSt_hi, c.iSt_lo);
+    const float qf = resid ? scale2(scaled_exp2(ld, c.Md, c.c_hi, c.c_lo), c.iSd_hi, c.iSd_lo) : 0.0f;
     if (fmaxf(pf, qf) > 0x1p-9f) return mass_f64(lt, ld, c, resid);
     return (double)fmaxf(pf - qf, 0.0f);
 }
@@ -1147,8 +1155,8 @@ __device__ __forceinline__ double run_mass(const float (&lt)[RUN], const float (
     float big = 0.0f;
 #pragma unroll
     for (int i = 0; i < RUN; ++i) {
-        const float pf = scaled_exp2(lt[i], c.Mt, c.c_hi, c.c_lo) * c.invSt;
-        const float qf = resid ? scaled_exp2(ld[i], c.Md, c.c_hi, c.c_lo) * c.invSd : 0.0f;
+        const float pf = scale2(scaled_exp2(lt[i], c.Mt, c.c_hi, c.c_lo), c.iSt_hi, c.iSt_lo);
+        const float qf = resid ? scale2(scaled_exp2(ld[i], c.Md, c.c_hi, c.c_lo), c.iSd_hi, c.iSd_lo) : 0.0f;
         big = fmaxf(big, fmaxf(pf, qf));
         acc += (double)fmaxf(pf - qf, 0.0f);
     }
@@ -1371,8 +1379,9 @@ __global__ __launch_bounds__(kThreads) void sv_draw_kernel(Params p, Work w)
                 if (slow) {
                     m[i] = draw_mass(lt[i], ld[i], c, resid);
                 } else {
-                    const float pf = scaled_exp2(lt[i], c.Mt, c.c_hi, c.c_lo) * c.invSt;
-                    const float qf = resid ? scaled_exp2(ld[i], c.Md, c.c_hi, c.c_lo) * c.invSd : 0.0f;
+                    const float pf = scale2(scaled_exp2(lt[i], c.Mt, c.c_hi, c.c_lo), c.iSt_hi, c.iSt_lo);
+                    const float qf =
+                        resid ? scale2(scaled_exp2(ld[i], c.Md, c.c_hi, c.c_lo), c.iSd_hi, c.iSd_lo) : 0.0f;
                     m[i] = (double)fmaxf(pf - qf, 0.0f);
                 }
                 if (m[i] > 0.0) lastpos = i0 + i;

@@ -409,3 +409,36 @@ def test_accept_margin_is_flagged():
     assert abs(float(u[0, 0]) - ratio) < 1e-6
     r = O.verify(t, d, np.array([[x]], np.int32), u, 1.0, dtype=F32)
     assert r.margin[0] & O.MARGIN_ACCEPT
+
+
+@pytest.mark.parametrize("noise", [0.01, 1.0])
+def test_cdf_gap_is_relative_to_residual_mass_with_a_floor(noise):
+    # The final draw's CDF gap (distance of w = u Z to the nearest step of
+    # cumsum(max(0, p - q))) is reported relative to max(Z, 0.1); nearly equal
+    # rows (noise 0.01) give Z well below 0.1, unequal rows (noise 1) above it.
+    rng = _rng(17)
+    B, K, V = 60, 1, 300
+    t, d, _, u = _problem(rng, B, K, V, noise=noise)
+    tok = np.zeros((B, K), np.int32)
+    for b in range(B):
+        p = special.softmax(t[b, 0].astype(np.float64))
+        q = special.softmax(d[b, 0].astype(np.float64))
+        tok[b, 0] = int(np.argmin(p / q))    # p(x) < q(x): ratio below 1
+    u[:, 0] = 1 - 2 ** -24                  # so the position is rejected
+    r = O.verify(t, d, tok, u, 1.0, dtype=F32)
+    zs = []
+    for b in range(B):
+        assert r.final_kind[b] == O.FINAL_RESIDUAL
+        p = special.softmax(t[b, 0].astype(np.float64))
+        q = special.softmax(d[b, 0].astype(np.float64))
+        res = np.maximum(p - q, 0.0)
+        C = np.cumsum(res)
+        Z = C[-1]
+        w = np.float64(u[b, K]) * Z
+        y = int(np.searchsorted(C, w, side="right"))
+        gap = min(abs(w - (C[y - 1] if y > 0 else 0.0)), abs(C[y] - w))
+        np.testing.assert_allclose(r.cdf_gap[b], gap / max(Z, 0.1), rtol=1e-6, atol=1e-15)
+        assert bool(r.margin[b] & O.MARGIN_CDF) == (gap / max(Z, 0.1) < 1e-6)
+        zs.append(Z)
+    zs = np.array(zs)
+    assert (zs < 0.1).all() if noise < 0.1 else (zs > 0.1).all()
