@@ -17,23 +17,25 @@
 //   sv_rows    one workgroup per 16384-element split of every row the group
 //              needs (target and draft rows of sequences still open), reduced
 //              to (max, sum exp2) or (max, argmax) partials.  No atomics and no
-//              fences: the kernel boundary publishes the partials.
-//   sv_decide  one wavefront per open sequence: merges the partials of the
+//              fences: the kernel boundary publishes the partials.  The last
+//              group from the fourth on, where few sequences are still open,
+//              runs as sv_rows_late (eight candidate rows per workgroup).
+//   sv_decide  one workgroup per open sequence: merges the partials of the
 //              group's positions in fp64 and walks them in order -- survival
 //              and verify length, the acceptance test u < p/q (or the greedy
 //              match) -- until the first rejection, the bonus row, or the end of
 //              the group.
 // Rows inside a group past a rejection are read speculatively (they lie within
 // the verify window).  Synchronising only at kernel boundaries keeps every
-// launch a pure stream: cross-XCD fences and hot atomics cost microseconds
-// each on this chip.
+// launch a pure stream: an agent-scope fence costs ~130 ns, serialised, on
+// this chip, so work is never handed between workgroups inside a launch.
 //
 // After the last group:
-//   sv_resid   per (rejecting sequence, split): sum of max(0, p - q) over the
-//              split of the rejected row pair.
+//   sv_resid   per (rejecting sequence, split, quarter split): segment sums of
+//              max(0, p - q) over the rejected row pair.
 //   sv_draw    per sequence: inverse-CDF draw (replacement or bonus) by split
-//              prefix in fp64, then one split re-read and scanned in token
-//              order; writes the outputs.
+//              and segment prefix in fp64, then one segment's tokens scanned
+//              in token order; writes the outputs.
 // sv_plan (first) sets up per-sequence state and the verify length where it
 // is known without reading logits.
 //
@@ -41,7 +43,8 @@
 // one fma per element, l*c - round(m*c) with c = log2(e)/T in fp32, and keep
 // the exact rounding error of m*c beside the split sum for the fp64 merges;
 // the final draw forms a = (l - m) * log2(e)/T with the constant split in two
-// fp32 parts (no systematic scale bias).  v_exp_f32 measured on MI355X:
+// fp32 parts and scales by the rows' 1/S in two fp32 parts (no systematic scale
+// bias, which would not cancel in p - q).  v_exp_f32 measured on MI355X:
 // < 0.8 ulp for arguments >= -12.  Sums run in fp32 over 8 elements and in
 // fp64 beyond, so a row sum carries ~1e-8 relative error.
 // Decisions (acceptance ratio, survival product, CDF prefix) are taken in fp64.
