@@ -68,7 +68,7 @@ def _compare(name, g, o):
 @pytest.fixture(scope="module")
 def sv():
     B = _B()
-    h = B.SpecVerify(4096, 16, 1024, B.SV_BF16, 0)
+    h = B.SpecVerify(4096, 256, 1024, B.SV_BF16, 0)
     yield h
     h.close()
 
@@ -97,7 +97,7 @@ def test_ties_zeros_and_certain_positions(sv):
     _compare("ties constant", _run_sched(sv, conf, speed), O.schedule(conf, speed))
 
 
-@pytest.mark.parametrize("Bn,K", [(1, 1), (1, 16), (3, 5), (1000, 7), (4096, 16)])
+@pytest.mark.parametrize("Bn,K", [(1, 1), (1, 16), (3, 5), (1000, 7), (4096, 16), (7, 32), (100, 33), (40, 256)])
 def test_shapes(sv, Bn, K):
     rng = np.random.default_rng(Bn * 31 + K)
     conf = rng.uniform(0.0, 1.0, size=(Bn, K)).astype(np.float32) ** 0.3
