@@ -31,7 +31,7 @@
 // this chip, so work is never handed between workgroups inside a launch.
 //
 // After the last group:
-//   sv_resid   per (rejecting sequence, split, quarter split): segment sums of
+//   sv_resid   per (rejecting sequence, split, half split): segment sums of
 //              max(0, p - q) over the rejected row pair.
 //   sv_draw    per sequence: inverse-CDF draw (replacement or bonus) by split
 //              and segment prefix in fp64, then one segment's tokens scanned
@@ -383,10 +383,10 @@ struct Chunk<SV_F32> {
     }
 };
 
-// A quarter of a split (kParts parts): loads q NL .. q NL + NL - 1 of the
-// split layout above, 16 elements per lane.  Element e of the part is element
-// q PER + e of the lane's split elements.
-constexpr int kParts = 4;
+// A part of a split (one of kParts): loads q NL .. q NL + NL - 1 of the
+// split layout above, kPerLane / kParts elements per lane.  Element e of the
+// part is element q PER + e of the lane's split elements.
+constexpr int kParts = 2;
 
 template <int DT>
 struct Part;
@@ -1211,10 +1211,10 @@ __device__ __forceinline__ void split_segments(const Chunk<DT>& tc, const Chunk<
     }
 }
 
-// One workgroup per (sequence, split, quarter of the split): the residual mass
-// of each of the quarter's segments (w.seg).  Quarters keep the workgroups
-// short and light on registers; the pass is compute-bound (two exponentials
-// per token).
+// One workgroup per (sequence, split, half of the split): the residual mass of
+// each of the half's segments (w.seg).  Halves (32 tokens per lane) keep the
+// workgroups short and balance the compute-bound pass (two exponentials per
+// token) better than whole splits; quarters and eighths measured slower.
 template <int DT, bool VEC, int MODE>
 __global__ __launch_bounds__(kThreads) void sv_resid_kernel(Params p, Work w)
 {
@@ -1233,7 +1233,7 @@ __global__ __launch_bounds__(kThreads) void sv_resid_kernel(Params p, Work w)
     tc.template load<VEC>(seq_row<DT, PK>(p.t, p.toff, p.tbs, p.trs, b, st.js - 1), split * kSplit, p.V, t, q);
     if (OH) {
         // the one-hot draft row, built in registers: logit 0 at the drafted
-        // token (held by one lane of one quarter of one split), -inf elsewhere
+        // token (held by one lane of one part of one split), -inf elsewhere
         const int x = p.tok[(long long)b * p.K + (st.js - 1)];
         const int off = x - split * kSplit;
         dc.one_hot(off >= 0 && off < kSplit ? Part<DT>::owned(off, q, t) : -1);
