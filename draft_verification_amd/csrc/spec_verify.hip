@@ -1303,7 +1303,7 @@ __global__ __launch_bounds__(kThreads) void sv_draw_kernel(Params p, Work w)
     float zrep = NAN, py = NAN;
 
     if (kind == KIND_RESID || kind == KIND_BONUS) {
-        if (kind == KIND_RESID) {
+        if (kind == KIND_RESID && !OH) {
             // every segment sum of the sequence at once (one round trip): the
             // split totals and the search inside the chosen split both read LDS
             const double* sg = w.seg + (long long)b * p.nsplit * kSegStride;
@@ -1315,10 +1315,26 @@ __global__ __launch_bounds__(kThreads) void sv_draw_kernel(Params p, Work w)
         if (tid < 64) {
             bool resid = kind == KIND_RESID;
             double m = 0.0;
-            if (resid && lane < p.nsplit) {
+            if (resid && !OH && lane < p.nsplit) {
                 // residual mass of split `lane`: its segments summed in order
 #pragma unroll 8
                 for (int g = 0; g < S::SEGS; ++g) m += s_all[lane * S::SEGS + g];
+            }
+            if (resid && OH) {
+                // one-hot drafts (no residual pass): the residual is p without
+                // x, so split `lane` carries its mass of p, less p(x) in the
+                // split holding x
+                const int x = p.tok[(long long)b * K + (st.js - 1)];
+                const void* trow = seq_row<DT, PK>(p.t, p.toff, p.tbs, p.trs, b, st.js - 1);
+                const double px =
+                    exp2_f64(((double)load_one<DT>(trow, x) - (double)st.Mt) * p.c64) / st.St;
+                if (lane < p.nsplit) {
+                    const long long pb = part_index(p, b, st.js - 1) + lane;
+                    const float mk = w.part_m[pb];
+                    if (mk != -INFINITY)
+                        m = w.part_s[pb] * exp2_f64(((double)mk - (double)st.Mt) * p.c64 - (double)w.part_d[pb]) / st.St;
+                    if (x / kSplit == lane) m = fmax(m - px, 0.0);
+                }
             }
             const double Z = __shfl(wave_incl_scan(m, lane), p.nsplit - 1);
             if (resid && !(Z > 0.0)) resid = false; // cannot happen in exact arithmetic after a rejection
@@ -1354,12 +1370,26 @@ __global__ __launch_bounds__(kThreads) void sv_draw_kernel(Params p, Work w)
         const int xone = (resid && OH) ? p.tok[(long long)b * K + (st.js - 1)] : -1; // one-hot draft token
 
         // 2. segment sums of that split: stored by sv_resid for a replacement
-        //    (already in LDS), computed here for a bonus draw
-        const double* s_seg = resid ? s_all + ks * S::SEGS : s_bonus;
-        if (!resid) {
+        //    (already in LDS), computed here for a bonus draw and for a
+        //    one-hot replacement (the draft row built in registers)
+        const double* s_seg = (resid && !OH) ? s_all + ks * S::SEGS : s_bonus;
+        if (!resid || OH) {
             Chunk<DT> tc;
             tc.template load<VEC>(trow, ks * kSplit, p.V, tid);
-            split_segments<DT>(tc, tc, c, false, s_bonus);
+            if (resid) {
+                const int off = xone - ks * kSplit;
+                int e = -1;
+                if (off >= 0 && off < kSplit) {
+                    int ol, oe;
+                    Chunk<DT>::owner(off, ol, oe);
+                    if (tid == ol) e = oe;
+                }
+                Chunk<DT> dc;
+                dc.one_hot(e);
+                split_segments<DT>(tc, dc, c, true, s_bonus);
+            } else {
+                split_segments<DT>(tc, tc, c, false, s_bonus);
+            }
             __syncthreads();
         }
 
@@ -1730,7 +1760,7 @@ void enqueue_step(const spec_verify* h, const Params& p, hipStream_t s, Mark& ma
         mark(K_DECIDE, 1);
     }
     mark(K_RESID, 0);
-    if (!GR)
+    if (!GR && !OH) // (one-hot drafts: the final draw forms p without x itself)
         hipLaunchKernelGGL((sv_resid_kernel<DT, VEC, MODE>), dim3(B * (unsigned)p.nsplit * kParts), dim3(kThreads), 0,
                            s, p, h->w);
     mark(K_RESID, 1);
