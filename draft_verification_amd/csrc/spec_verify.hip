@@ -103,6 +103,7 @@ struct Work {
     float* part_d;    // same layout, the d of that sum (the true split sum is part_s * 2^-d)
     int* part_i;      // same layout, split argmax (greedy)
     SeqState* st;     // [max_batch]
+    SeqState* fin;    // [max_batch] state after the last group, stored by sv_resid (which takes its decisions)
     int* live;        // [max_batch] (L + 1) << 2 | flags, the part of st that sv_rows reads
     double* seg;      // [max_batch][nsplit][64] residual mass per segment of a split
     float* xlog;      // [max_batch][2K+1] logit of the drafted token in each row
@@ -879,18 +880,39 @@ __device__ __forceinline__ void seg_argmax(float& v, int& i, int sw)
     }
 }
 
+struct DecideSmem {
+    float sMt[kMaxGroup], sMd[kMaxGroup], sLt[kMaxGroup], sLd[kMaxGroup];
+    double sSt[kMaxGroup], sSd[kMaxGroup];
+    int sG[kMaxGroup];
+    double sRatio[kMaxGroup];
+    float sLseT[kMaxGroup], sLseD[kMaxGroup];
+    int sTok[kMaxGroup];
+    float sU[kMaxGroup];
+    SeqState st;
+};
+
+// The decisions of sequence b over positions j0 .. j0+G-1, from the state
+// before the group (w.st); every thread of the workgroup calls it and gets the
+// state after the group, which the caller stores.  writer: this workgroup
+// writes the decisions' outputs (lse and survival rows, status bits); other
+// callers only learn the result.
 template <int DT, bool GREEDY, int MODE>
-__global__ __launch_bounds__(kThreads) void sv_decide_kernel(Params p, Work w, int j0, int G)
+__device__ SeqState decide_group(const Params& p, const Work& w, int b, int j0, int G, bool writer, DecideSmem& sm)
 {
     constexpr bool OH = (MODE & MODE_ONEHOT) != 0;
-    __shared__ float sMt[kMaxGroup], sMd[kMaxGroup], sLt[kMaxGroup], sLd[kMaxGroup];
-    __shared__ double sSt[kMaxGroup], sSd[kMaxGroup];
-    __shared__ int sG[kMaxGroup];
-    __shared__ double sRatio[kMaxGroup];
-    __shared__ float sLseT[kMaxGroup], sLseD[kMaxGroup];
-    __shared__ int sTok[kMaxGroup];
-    __shared__ float sU[kMaxGroup];
-    const int b = blockIdx.x, tid = threadIdx.x, K = p.K;
+    float* const sMt = sm.sMt;
+    float* const sMd = sm.sMd;
+    float* const sLt = sm.sLt;
+    float* const sLd = sm.sLd;
+    double* const sSt = sm.sSt;
+    double* const sSd = sm.sSd;
+    int* const sG = sm.sG;
+    double* const sRatio = sm.sRatio;
+    float* const sLseT = sm.sLseT;
+    float* const sLseD = sm.sLseD;
+    int* const sTok = sm.sTok;
+    float* const sU = sm.sU;
+    const int tid = threadIdx.x, K = p.K;
     const int n = min(j0 + G - 1, K + 1) - j0 + 1;
     const int sw = p.seg_w;
     const int per = 2 * n * sw;
@@ -928,7 +950,7 @@ __global__ __launch_bounds__(kThreads) void sv_decide_kernel(Params p, Work w, i
     }
     const float tau_b = (!GREEDY && p.derived) ? p.tau[b] : 0.0f;
     const int flags0 = st0.flags, L0 = st0.L;
-    if (!(flags0 & (FL_ACC | FL_LEN))) return;
+    if (!(flags0 & (FL_ACC | FL_LEN))) return st0; // (the same in every thread)
     for (int base = 0; base < per; base += kThreads) {
         const int t = base + tid;
         const int pk = t / sw, k = t % sw;
@@ -1003,8 +1025,7 @@ __global__ __launch_bounds__(kThreads) void sv_decide_kernel(Params p, Work w, i
         }
     }
     __syncthreads();
-    if (tid != 0) return;
-
+    if (tid == 0) {
     SeqState st = st0;
     bool acc = (flags0 & FL_ACC) != 0;
     bool len = (flags0 & FL_LEN) != 0;
@@ -1014,13 +1035,13 @@ __global__ __launch_bounds__(kThreads) void sv_decide_kernel(Params p, Work w, i
         st.rows += (target_row_needed(flags0, L0, j, K) ? 1 : 0) + ((dread && !OH) ? 1 : 0);
         if (!acc && !len) continue; // rows of this group past the stop were still streamed
         if (!GREEDY) {
-            if (acc && p.lse_t) p.lse_t[(long long)b * (K + 1) + (j - 1)] = sLseT[q];
-            if (dread && p.lse_d && !OH) p.lse_d[(long long)b * K + (j - 1)] = sLseD[q];
+            if (writer && acc && p.lse_t) p.lse_t[(long long)b * (K + 1) + (j - 1)] = sLseT[q];
+            if (writer && dread && p.lse_d && !OH) p.lse_d[(long long)b * K + (j - 1)] = sLseD[q];
             if (dread && p.derived && !OH) {
                 // c_j = max_v q_j(v) = 1 / Sd; S_j = S_{j-1} c_j
                 const double S = st.S / sSd[q];
                 st.S = S;
-                if (p.surv) p.surv[(long long)b * K + (j - 1)] = (float)S;
+                if (writer && p.surv) p.surv[(long long)b * K + (j - 1)] = (float)S;
                 if (len) {
                     if (S >= (double)tau_b) {
                         if (j == K) { st.L = K; len = false; }
@@ -1039,7 +1060,7 @@ __global__ __launch_bounds__(kThreads) void sv_decide_kernel(Params p, Work w, i
                 st.kind = KIND_BAD;
                 st.a = 0;
                 acc = false;
-                or_status(&w.ctl[CTL_STATUS], SV_STATUS_BAD_INPUT);
+                if (writer) or_status(&w.ctl[CTL_STATUS], SV_STATUS_BAD_INPUT);
             } else if (GREEDY) {
                 if (x == sG[q]) {
                     st.a = j;
@@ -1074,8 +1095,23 @@ __global__ __launch_bounds__(kThreads) void sv_decide_kernel(Params p, Work w, i
         }
     }
     st.flags = (acc ? FL_ACC : 0) | (len ? FL_LEN : 0);
-    w.st[b] = st;
-    w.live[b] = st.flags ? (((st.L + 1) << 2) | st.flags) : 0;
+    sm.st = st;
+    }
+    __syncthreads();
+    return sm.st;
+}
+
+// One workgroup per sequence.
+template <int DT, bool GREEDY, int MODE>
+__global__ __launch_bounds__(kThreads) void sv_decide_kernel(Params p, Work w, int j0, int G)
+{
+    __shared__ DecideSmem sm;
+    const int b = (int)blockIdx.x;
+    const SeqState st = decide_group<DT, GREEDY, MODE>(p, w, b, j0, G, true, sm);
+    if (threadIdx.x == 0) {
+        w.st[b] = st;
+        w.live[b] = st.flags ? (((st.L + 1) << 2) | st.flags) : 0;
+    }
 }
 
 // ---------------------------------------------------------------- final draw
@@ -1211,22 +1247,29 @@ __device__ __forceinline__ void split_segments(const Chunk<DT>& tc, const Chunk<
     }
 }
 
-// One workgroup per (sequence, split, half of the split): the residual mass of
-// each of the half's segments (w.seg).  Halves (32 tokens per lane) keep the
-// workgroups short and balance the compute-bound pass (two exponentials per
-// token) better than whole splits; quarters and eighths measured slower.
+// One workgroup per (sequence, split, half of the split): first the decisions
+// of the last position group (positions j0 .. j0+G-1), taken by each of the
+// sequence's workgroups from the group's partials (the one of split 0, half 0
+// writes the outputs and w.fin), then, if they end in a rejection, the
+// residual mass of each of the half's segments (w.seg).  Taking the last
+// decisions here saves a launch and its drain.  Halves (32 tokens per lane) keep
+// the workgroups short and balance the compute-bound pass (two exponentials
+// per token) better than whole splits; quarters and eighths measured slower.
 template <int DT, bool VEC, int MODE>
-__global__ __launch_bounds__(kThreads) void sv_resid_kernel(Params p, Work w)
+__global__ __launch_bounds__(kThreads) void sv_resid_kernel(Params p, Work w, int j0, int G)
 {
     constexpr bool OH = (MODE & MODE_ONEHOT) != 0, PK = (MODE & MODE_PACKED) != 0;
     using S = Seg<DT>;
     constexpr int NL = Part<DT>::NL, QSEG = NL * kWaves;
     __shared__ double s_seg[QSEG];
+    __shared__ DecideSmem sm;
     const int q = (int)(blockIdx.x % kParts);
     const int split = (int)((blockIdx.x / kParts) % p.nsplit);
     const int b = (int)(blockIdx.x / kParts / p.nsplit);
-    if (w.st[b].kind != KIND_RESID) return;
-    const SeqState st = w.st[b];
+    const bool writer = split == 0 && q == 0;
+    const SeqState st = decide_group<DT, false, MODE & MODE_ONEHOT>(p, w, b, j0, G, writer, sm);
+    if (writer && threadIdx.x == 0) w.fin[b] = st;
+    if (st.kind != KIND_RESID) return;
     const DrawCtx c = make_ctx(st, p);
     const int t = (int)threadIdx.x, lane = t & 63, wv = t >> 6;
     Part<DT> tc, dc;
@@ -1281,8 +1324,10 @@ __device__ __forceinline__ int wave_last_positive(double v, int n)
     return pos ? 63 - __clzll(pos) : -1;
 }
 
+// sts: the states after the last group (w.fin when sv_resid took the last
+// decisions, else w.st).
 template <int DT, bool VEC, int MODE>
-__global__ __launch_bounds__(kThreads) void sv_draw_kernel(Params p, Work w)
+__global__ __launch_bounds__(kThreads) void sv_draw_kernel(Params p, Work w, const SeqState* __restrict__ sts)
 {
     constexpr bool OH = (MODE & MODE_ONEHOT) != 0, PK = (MODE & MODE_PACKED) != 0;
     using S = Seg<DT>;
@@ -1296,7 +1341,7 @@ __global__ __launch_bounds__(kThreads) void sv_draw_kernel(Params p, Work w)
     // drafted tokens this thread copies to the output
     const float uf32 = (p.u == nullptr) ? 0.0f : p.u[(long long)b * (K + 1) + K];
     const int tok0 = tid < K ? p.tok[(long long)b * K + tid] : -1;
-    const SeqState st = w.st[b];
+    const SeqState st = sts[b];
     int kind = st.kind;
     int a = st.a;
     int y = -1;
@@ -1743,6 +1788,9 @@ void enqueue_step(const spec_verify* h, const Params& p, hipStream_t s, Mark& ma
     mark(K_PLAN, 0);
     hipLaunchKernelGGL(sv_plan_kernel, dim3((B + kThreads - 1) / kThreads), dim3(kThreads), 0, s, p, h->w);
     mark(K_PLAN, 1);
+    // With a residual pass (sampling with draft probabilities) that pass takes
+    // the last group's decisions; otherwise each group has its own launch.
+    constexpr bool FUSED_LAST = !GR && !OH;
     for (int g = 0; g < ng; ++g) {
         const long long nrow = (long long)B * slots(g);
         mark(K_ROWS, 0);
@@ -1754,19 +1802,20 @@ void enqueue_step(const spec_verify* h, const Params& p, hipStream_t s, Mark& ma
             hipLaunchKernelGGL((sv_rows_kernel<DT, VEC, GR, MODE>), dim3((unsigned)(nrow * p.nsplit)), dim3(kThreads),
                                0, s, p, h->w, gj[g], gn[g]);
         mark(K_ROWS, 1);
+        if (FUSED_LAST && g + 1 == ng) break;
         mark(K_DECIDE, 0);
         hipLaunchKernelGGL((sv_decide_kernel<DT, GR, MODE & MODE_ONEHOT>), dim3(B), dim3(kThreads), 0, s, p, h->w,
                            gj[g], gn[g]);
         mark(K_DECIDE, 1);
     }
     mark(K_RESID, 0);
-    if (!GR && !OH) // (one-hot drafts: the final draw forms p without x itself)
+    if (FUSED_LAST) // (one-hot drafts: the final draw forms p without x itself)
         hipLaunchKernelGGL((sv_resid_kernel<DT, VEC, MODE>), dim3(B * (unsigned)p.nsplit * kParts), dim3(kThreads), 0,
-                           s, p, h->w);
+                           s, p, h->w, gj[ng - 1], gn[ng - 1]);
     mark(K_RESID, 1);
     mark(K_DRAW, 0);
     hipLaunchKernelGGL((sv_draw_kernel<DT, VEC, MODE>), dim3(B), dim3(kThreads),
-                       (size_t)p.nsplit * Seg<DT>::SEGS * sizeof(double), s, p, h->w);
+                       (size_t)p.nsplit * Seg<DT>::SEGS * sizeof(double), s, p, h->w, FUSED_LAST ? h->w.fin : h->w.st);
     mark(K_DRAW, 1);
 }
 
@@ -1895,6 +1944,7 @@ int spec_verify_create(const spec_verify_config* cfg, spec_verify_t** out)
     const size_t o_pi = off; off = align_up(off + nrow * ns * sizeof(int));
     const size_t o_pd = off; off = align_up(off + nrow * ns * sizeof(float));
     const size_t o_st = off; off = align_up(off + (size_t)cfg->max_batch * sizeof(SeqState));
+    const size_t o_fi = off; off = align_up(off + (size_t)cfg->max_batch * sizeof(SeqState));
     const size_t o_lv = off; off = align_up(off + (size_t)cfg->max_batch * sizeof(int));
     const size_t o_sg = off; off = align_up(off + (size_t)cfg->max_batch * ns * kSegStride * sizeof(double));
     const size_t o_xl = off; off = align_up(off + nrow * sizeof(float));
@@ -1914,6 +1964,7 @@ int spec_verify_create(const spec_verify_config* cfg, spec_verify_t** out)
     h->w.part_d = (float*)(base + o_pd);
     h->w.part_i = (int*)(base + o_pi);
     h->w.st = (SeqState*)(base + o_st);
+    h->w.fin = (SeqState*)(base + o_fi);
     h->w.live = (int*)(base + o_lv);
     h->w.seg = (double*)(base + o_sg);
     h->w.xlog = (float*)(base + o_xl);
