@@ -253,9 +253,9 @@ def time_admission(sv, torch, B, synth, Bn, K, steps, warmup):
             "inputs": "confidences uniform in [0.3, 1) (Philox key 500), step time 20 + 0.05 n"}
 
 
-def copy_calibration():
-    import torch
-    n = 1 << 30
+def copy_rate(torch, n=1 << 30, reps=10):
+    """A plain device copy of n bytes (torch's copy kernel): bytes read and
+    written per ms, a measured ceiling beside the published 8 TB/s."""
     src = torch.empty(n, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
     src.fill_(1)
@@ -265,13 +265,18 @@ def copy_calibration():
     torch.cuda.synchronize()
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     s.record()
-    reps = 10
     for _ in range(reps):
         dst.copy_(src)
     e.record()
     torch.cuda.synchronize()
     ms = s.elapsed_time(e) / reps
-    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "ms": ms, "gbps_rw": 2 * n / ms / 1e6}))
+    del src, dst
+    return {"copy_bytes_read": n, "copy_bytes_written": n, "ms": ms, "gbps_rw": 2 * n / ms / 1e6}
+
+
+def copy_calibration():
+    import torch
+    print(json.dumps(copy_rate(torch)))
 
 
 def main():
@@ -347,6 +352,7 @@ def main():
     del dps, argv
     onehot = time_onehot(torch, B, D, synth, args.steps, args.warmup)
     packed = time_packed(torch, B, D, synth, args.steps, args.warmup)
+    ceiling = copy_rate(torch)
 
     L_total = [int(o["verify_len_out"].sum()) for o in outs]
     acc = [step_bytes(o, w) for o in outs]
@@ -386,6 +392,8 @@ def main():
                      "traffic_source": "rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated, bytes per step; null "
                                        "when the kernel source changed since the counters were taken"},
         "step_ms_distribution": step_dist,
+        "copy_ceiling": {"gbps_rw": ceiling["gbps_rw"], "bytes": 2 * ceiling["copy_bytes_read"],
+                         "what": "torch device copy of 1 GiB, (read + write bytes) / time; sv_rows only reads"},
         "step_hbm_gbps": bytes_step / (ms_step / 1e3) / 1e9,
         "emitted_tokens_per_s": float(np.mean([o["accepted_len"].sum() + w.B for o in outs])) / (ms_step / 1e3),
         "mean_accepted": mean_a,

@@ -397,20 +397,6 @@ struct Part<SV_BF16> {
     static constexpr int NL = 8 / kParts, PER = 8 * NL;
     uint32_t w[PER / 2];
     __device__ __forceinline__ float get(int e) const { return (e & 1) ? bf16_hi(w[e >> 1]) : bf16_lo(w[e >> 1]); }
-    // element of this lane's part holding split offset off, or -1
-    __device__ __forceinline__ static int owned(int off, int q, int lane)
-    {
-        const int k = off >> 11;
-        return ((off >> 3) & 255) == lane && k / NL == q ? (k % NL) * 8 + (off & 7) : -1;
-    }
-    __device__ __forceinline__ void one_hot(int e)
-    {
-#pragma unroll
-        for (int k = 0; k < PER / 2; ++k) {
-            const uint32_t lo = 2 * k == e ? 0x0000u : 0xFF80u, hi = 2 * k + 1 == e ? 0x0000u : 0xFF80u;
-            w[k] = lo | (hi << 16);
-        }
-    }
     template <bool VEC>
     __device__ __forceinline__ void load(const void* row, int base, int V, int lane, int q)
     {
@@ -443,16 +429,6 @@ struct Part<SV_F32> {
     static constexpr int NL = 16 / kParts, PER = 4 * NL;
     float w[PER];
     __device__ __forceinline__ float get(int e) const { return w[e]; }
-    __device__ __forceinline__ static int owned(int off, int q, int lane)
-    {
-        const int k = off >> 10;
-        return ((off >> 2) & 255) == lane && k / NL == q ? (k % NL) * 4 + (off & 3) : -1;
-    }
-    __device__ __forceinline__ void one_hot(int e)
-    {
-#pragma unroll
-        for (int k = 0; k < PER; ++k) w[k] = k == e ? 0.0f : -INFINITY;
-    }
     template <bool VEC>
     __device__ __forceinline__ void load(const void* row, int base, int V, int lane, int q)
     {
@@ -1258,7 +1234,8 @@ __device__ __forceinline__ void split_segments(const Chunk<DT>& tc, const Chunk<
 template <int DT, bool VEC, int MODE>
 __global__ __launch_bounds__(kThreads) void sv_resid_kernel(Params p, Work w, int j0, int G)
 {
-    constexpr bool OH = (MODE & MODE_ONEHOT) != 0, PK = (MODE & MODE_PACKED) != 0;
+    static_assert((MODE & MODE_ONEHOT) == 0, "one-hot drafts have no residual pass");
+    constexpr bool PK = (MODE & MODE_PACKED) != 0;
     using S = Seg<DT>;
     constexpr int NL = Part<DT>::NL, QSEG = NL * kWaves;
     __shared__ double s_seg[QSEG];
@@ -1267,22 +1244,14 @@ __global__ __launch_bounds__(kThreads) void sv_resid_kernel(Params p, Work w, in
     const int split = (int)((blockIdx.x / kParts) % p.nsplit);
     const int b = (int)(blockIdx.x / kParts / p.nsplit);
     const bool writer = split == 0 && q == 0;
-    const SeqState st = decide_group<DT, false, MODE & MODE_ONEHOT>(p, w, b, j0, G, writer, sm);
+    const SeqState st = decide_group<DT, false, 0>(p, w, b, j0, G, writer, sm);
     if (writer && threadIdx.x == 0) w.fin[b] = st;
     if (st.kind != KIND_RESID) return;
     const DrawCtx c = make_ctx(st, p);
     const int t = (int)threadIdx.x, lane = t & 63, wv = t >> 6;
     Part<DT> tc, dc;
     tc.template load<VEC>(seq_row<DT, PK>(p.t, p.toff, p.tbs, p.trs, b, st.js - 1), split * kSplit, p.V, t, q);
-    if (OH) {
-        // the one-hot draft row, built in registers: logit 0 at the drafted
-        // token (held by one lane of one part of one split), -inf elsewhere
-        const int x = p.tok[(long long)b * p.K + (st.js - 1)];
-        const int off = x - split * kSplit;
-        dc.one_hot(off >= 0 && off < kSplit ? Part<DT>::owned(off, q, t) : -1);
-    } else {
-        dc.template load<VEC>(seq_row<DT, PK>(p.d, p.doff, p.dbs, p.drs, b, st.js - 1), split * kSplit, p.V, t, q);
-    }
+    dc.template load<VEC>(seq_row<DT, PK>(p.d, p.doff, p.dbs, p.drs, b, st.js - 1), split * kSplit, p.V, t, q);
 #pragma unroll
     for (int k = 0; k < NL; ++k) {
         float lt[S::RUN], ld[S::RUN];
@@ -1809,7 +1778,7 @@ void enqueue_step(const spec_verify* h, const Params& p, hipStream_t s, Mark& ma
         mark(K_DECIDE, 1);
     }
     mark(K_RESID, 0);
-    if (FUSED_LAST) // (one-hot drafts: the final draw forms p without x itself)
+    if constexpr (FUSED_LAST) // (one-hot drafts: the final draw forms p without x itself)
         hipLaunchKernelGGL((sv_resid_kernel<DT, VEC, MODE>), dim3(B * (unsigned)p.nsplit * kParts), dim3(kThreads), 0,
                            s, p, h->w, gj[ng - 1], gn[ng - 1]);
     mark(K_RESID, 1);
