@@ -1848,10 +1848,14 @@ static int check_config(const spec_verify_config* cfg)
     if (cfg->vocab < 1 || cfg->vocab > SV_MAX_VOCAB) return SV_EINVAL;
     if (cfg->dtype != SV_F32 && cfg->dtype != SV_BF16) return SV_EUNSUPPORTED;
     if (cfg->device < 0) return SV_EINVAL;
-    const long long grid = (long long)cfg->max_batch * 2 * kMaxGroup * nsplit_of(cfg->vocab);
-    if (grid > 0x7fffffffll) return SV_EUNSUPPORTED; // largest sv_rows grid
-    const long long nres = (long long)cfg->max_batch * nsplit_of(cfg->vocab);
-    if (nres > 0x7fffffffll) return SV_EUNSUPPORTED;
+    // A launch's work-item count must fit in 32 bits.  The largest launches:
+    // sv_rows over the widest position group (at most min(kMaxGroup, K + 1)
+    // positions, a target and a draft row each) and sv_resid.
+    const long long ns = nsplit_of(cfg->vocab);
+    const long long gmax = std::min(kMaxGroup, cfg->max_draft + 1);
+    const long long rows_wg = (long long)cfg->max_batch * 2 * gmax * ns;
+    const long long resid_wg = (long long)cfg->max_batch * ns * kParts;
+    if (std::max(rows_wg, resid_wg) * kThreads > 0xffffffffll) return SV_EUNSUPPORTED;
     return SV_OK;
 }
 

@@ -102,7 +102,11 @@ enum { SV_LEN_FIXED = 0, SV_LEN_TAU = 1 };
 enum { SV_DRAFT_PROBS = 0, SV_DRAFT_ONEHOT = 1 };
 enum { SV_STATUS_BAD_INPUT = 1, SV_STATUS_TIMEOUT = 2 };
 
-/* Limits checked by spec_verify_create. */
+/* Limits checked by spec_verify_create.  Besides these, the largest launch of
+ * a configuration must stay within 2^32 - 1 work-items: max_batch *
+ * 2 * min(16, max_draft + 1) * ceil(vocab / 16384) workgroups of 256 (and
+ * max_batch * ceil(vocab / 16384) * 2 of them); larger configurations return
+ * SV_EUNSUPPORTED. */
 #define SV_MAX_VOCAB 1048576
 #define SV_MAX_BATCH 1048575
 #define SV_MAX_DRAFT 256

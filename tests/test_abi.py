@@ -107,6 +107,22 @@ def test_bad_configs_are_rejected_before_device_work(B, cfg):
     assert not h.value
 
 
+def test_launches_beyond_32_bit_work_item_counts_are_rejected(B):
+    # 1048575 sequences x 16-position groups x 8 splits: 2^28 workgroups of 256
+    c = B.Config(1048575, 16, 129280, B.SV_BF16, 0)
+    assert B.check(c, B.Args()) == B.SV_EUNSUPPORTED
+    h = ctypes.c_void_p()
+    assert B.lib().spec_verify_create(ctypes.byref(c), ctypes.byref(h)) == B.SV_EUNSUPPORTED
+    assert not h.value
+    # the same batch with K = 1 and one split stays within the bound (the
+    # configuration passes; the empty arguments are what is rejected)
+    c = B.Config(1048575, 1, 8, B.SV_F32, 0)
+    assert B.check(c, B.Args()) == B.SV_EINVAL
+    # at V = 129280 and K = 16 the bound allows 65535 sequences, not 65536
+    assert B.check(B.Config(65535, 16, 129280, B.SV_BF16, 0), B.Args()) == B.SV_EINVAL
+    assert B.check(B.Config(65536, 16, 129280, B.SV_BF16, 0), B.Args()) == B.SV_EUNSUPPORTED
+
+
 def test_destroy_null_is_a_no_op(B):
     assert B.lib().spec_verify_destroy(None) == B.SV_OK
 
