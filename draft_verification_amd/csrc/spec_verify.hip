@@ -1136,6 +1136,28 @@ __device__ __forceinline__ DrawCtx make_ctx(const SeqState& st, const Params& p)
     return c;
 }
 
+__device__ __forceinline__ float uniform_f32(float v) { return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v))); }
+
+__device__ __forceinline__ double uniform_f64(double v)
+{
+    const unsigned long long u = (unsigned long long)__double_as_longlong(v);
+    const unsigned lo = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)u);
+    const unsigned hi = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)(u >> 32));
+    return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+
+// The context of a workgroup-uniform state, held in scalar registers.
+__device__ __forceinline__ DrawCtx uniform_ctx(const DrawCtx& c)
+{
+    DrawCtx u;
+    u.Mt = uniform_f32(c.Mt); u.Md = uniform_f32(c.Md);
+    u.iSt_hi = uniform_f32(c.iSt_hi); u.iSt_lo = uniform_f32(c.iSt_lo);
+    u.iSd_hi = uniform_f32(c.iSd_hi); u.iSd_lo = uniform_f32(c.iSd_lo);
+    u.c_hi = uniform_f32(c.c_hi); u.c_lo = uniform_f32(c.c_lo);
+    u.iSt = uniform_f64(c.iSt); u.iSd = uniform_f64(c.iSd); u.c64 = uniform_f64(c.c64);
+    return u;
+}
+
 __device__ __forceinline__ double mass_f64(float lt, float ld, const DrawCtx& c, bool resid)
 {
     const double pd = exp2_f64(((double)lt - (double)c.Mt) * c.c64) * c.iSt;
@@ -1247,7 +1269,7 @@ __global__ __launch_bounds__(kThreads) void sv_resid_kernel(Params p, Work w, in
     const SeqState st = decide_group<DT, false, 0>(p, w, b, j0, G, writer, sm);
     if (writer && threadIdx.x == 0) w.fin[b] = st;
     if (st.kind != KIND_RESID) return;
-    const DrawCtx c = make_ctx(st, p);
+    const DrawCtx c = uniform_ctx(make_ctx(st, p));
     const int t = (int)threadIdx.x, lane = t & 63, wv = t >> 6;
     Part<DT> tc, dc;
     tc.template load<VEC>(seq_row<DT, PK>(p.t, p.toff, p.tbs, p.trs, b, st.js - 1), split * kSplit, p.V, t, q);
