@@ -111,6 +111,28 @@ def cpu_baseline(prob, L_total, seconds=10.0, max_reps=200):
                       f"in {el:.2f} s on the host CPU ({cpu_model})"}
 
 
+def cpu_single_thread(seconds=2.0):
+    """The oracle on one host thread for the two small workloads (tiny: B=4
+    K=4 V=1024 fp32; zipf64: B=64 K=8 V=129280 bf16), about `seconds` each."""
+    from oracle import oracle as O
+    from synth import synth
+    out = {}
+    for name in ("tiny", "zipf64"):
+        prob = synth.make_problem(synth.WORKLOADS[name])
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            r = O.verify_problem(prob, threads=1)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= seconds or reps >= 2000:
+                break
+        L = int(np.asarray(r.verify_len).sum())
+        w = prob.w
+        out[name] = {"us_per_step": el / reps * 1e6, "verified_positions_per_s": reps * L / el, "threads": 1,
+                     "B": w.B, "K": w.K, "V": w.V, "steps": reps}
+    return out
+
+
 def time_onehot(torch, B, D, synth, steps, warmup):
     """One-hot drafts (q_j = point mass at x_j; no draft logits handed over) on
     peaked rows where a greedy drafter is worth verifying: B=256 K=16 V=129280
@@ -410,6 +432,7 @@ def main():
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on the same workload ...")
         out["cpu_baseline"] = cpu_baseline(probs[0], L_total[0])
+        out["cpu_baseline"]["single_thread"] = cpu_single_thread()
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
