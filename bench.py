@@ -111,6 +111,26 @@ def cpu_baseline(prob, L_total, seconds=10.0, max_reps=200):
                       f"in {el:.2f} s on the host CPU ({cpu_model})"}
 
 
+def timed_inputs_check(probs, outs):
+    """The oracle on the exact inputs that were timed: emitted tokens, accepted
+    and verify lengths must match for every sequence outside the oracle's
+    margins (a margin sequence is counted, not compared)."""
+    from oracle import oracle as O
+    n = mism = margin = 0
+    for prob, g in zip(probs, outs):
+        orc = O.verify_problem(prob)
+        for i, b in enumerate(orc.seq):
+            n += 1
+            if int(orc.margin[i]) != 0:
+                margin += 1
+                continue
+            same = (int(g["accepted_len"][b]) == int(orc.accepted_len[i])
+                    and int(g["verify_len_out"][b]) == int(orc.verify_len[i])
+                    and np.array_equal(g["out_tokens"][b], orc.out_tokens[i]))
+            mism += 0 if same else 1
+    return {"sequences": n, "compared": n - margin, "margin_cases": margin, "mismatches": mism}
+
+
 def cpu_single_thread(seconds=2.0):
     """The oracle on one host thread for the two small workloads (tiny: B=4
     K=4 V=1024 fp32; zipf64: B=64 K=8 V=129280 bf16), about `seconds` each."""
@@ -433,6 +453,7 @@ def main():
         log("[bench] timing the CPU oracle on the same workload ...")
         out["cpu_baseline"] = cpu_baseline(probs[0], L_total[0])
         out["cpu_baseline"]["single_thread"] = cpu_single_thread()
+        out["cpu_baseline"]["timed_inputs_vs_oracle"] = timed_inputs_check(probs, outs)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
