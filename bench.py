@@ -439,6 +439,7 @@ def main():
         "step_hbm_gbps": bytes_step / (ms_step / 1e3) / 1e9,
         "emitted_tokens_per_s": float(np.mean([o["accepted_len"].sum() + w.B for o in outs])) / (ms_step / 1e3),
         "mean_accepted": mean_a,
+        "replacement_fraction": float(np.mean([(o["accepted_len"] < o["verify_len_out"]).mean() for o in outs])),
         "window_bytes_per_step": window_step,
         "first_rejection_bytes_per_step": needed_step,
         "rows_per_step": sum(a["rows"] for a in acc) / 2.0,
