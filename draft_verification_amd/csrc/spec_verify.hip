@@ -55,6 +55,7 @@
 // reproducible and independent of a sequence's batch position and of B.
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 
 #include <math.h>
 #include <stdint.h>
@@ -1750,6 +1751,30 @@ struct spec_verify {
 
 namespace {
 
+// Launches one kernel of a step (256 threads per workgroup) on stream s.  While
+// per-kernel timing is on, the start and stop events are attached to the
+// dispatch itself (hipExtLaunchKernelGGL), so they time the kernel's execution
+// and not the queue around it.
+struct StepLauncher {
+    const spec_verify* h;
+    hipStream_t s;
+    bool timing;
+    int slot;
+    template <typename F, typename... Args>
+    void operator()(int k, F kernel, dim3 grid, uint32_t shmem, Args... args)
+    {
+        if (timing && slot < kMaxSlots) {
+            const int idx = h->timing_n * kMaxSlots + slot;
+            hipExtLaunchKernelGGL(kernel, grid, dim3(kThreads), shmem, s, h->ev[idx * 2], h->ev[idx * 2 + 1], 0,
+                                  args...);
+            h->ev_kernel[idx] = k;
+            ++slot;
+        } else {
+            hipLaunchKernelGGL(kernel, grid, dim3(kThreads), shmem, s, args...);
+        }
+    }
+};
+
 // One verification step on stream s: plan, then per position group the row
 // statistics and the decisions, then the residual masses and the final draw.
 // Groups hold 3, 3, 4, 8, 16, 16, ... positions (a remainder of one position
@@ -1758,8 +1783,8 @@ namespace {
 // drain and the decisions), rows past a rejection inside a group are read for
 // nothing.  At B = 256, K = 16 with about 3.8 accepted positions per sequence
 // this schedule (3, 3, 4, 7) measured 4.5 us per step less than 2, 2, 4, 9.
-template <int DT, bool VEC, bool GR, int MODE, typename Mark>
-void enqueue_step(const spec_verify* h, const Params& p, hipStream_t s, Mark& mark)
+template <int DT, bool VEC, bool GR, int MODE, typename Launch>
+void enqueue_step(const spec_verify* h, const Params& p, hipStream_t s, Launch& launch)
 {
     constexpr bool OH = (MODE & MODE_ONEHOT) != 0;
     const unsigned B = (unsigned)p.B;
@@ -1776,38 +1801,26 @@ void enqueue_step(const spec_verify* h, const Params& p, hipStream_t s, Mark& ma
         j0 += G;
     }
     auto slots = [&](int g) { return (GR || OH) ? gn[g] : 2 * gn[g]; };
-    mark(K_PLAN, 0);
-    hipLaunchKernelGGL(sv_plan_kernel, dim3((B + kThreads - 1) / kThreads), dim3(kThreads), 0, s, p, h->w);
-    mark(K_PLAN, 1);
+    launch(K_PLAN, sv_plan_kernel, dim3((B + kThreads - 1) / kThreads), 0, p, h->w);
     // With a residual pass (sampling with draft probabilities) that pass takes
     // the last group's decisions; otherwise each group has its own launch.
     constexpr bool FUSED_LAST = !GR && !OH;
     for (int g = 0; g < ng; ++g) {
         const long long nrow = (long long)B * slots(g);
-        mark(K_ROWS, 0);
         if (VEC && g >= 3 && g + 1 == ng) // (the unaligned path keeps one row per workgroup)
-            hipLaunchKernelGGL((sv_rows_late_kernel<DT, true, GR, MODE>),
-                               dim3((unsigned)((nrow + kRowsLate - 1) / kRowsLate * p.nsplit)), dim3(kThreads), 0, s,
-                               p, h->w, gj[g], gn[g]);
+            launch(K_ROWS, sv_rows_late_kernel<DT, true, GR, MODE>,
+                   dim3((unsigned)((nrow + kRowsLate - 1) / kRowsLate * p.nsplit)), 0, p, h->w, gj[g], gn[g]);
         else
-            hipLaunchKernelGGL((sv_rows_kernel<DT, VEC, GR, MODE>), dim3((unsigned)(nrow * p.nsplit)), dim3(kThreads),
-                               0, s, p, h->w, gj[g], gn[g]);
-        mark(K_ROWS, 1);
+            launch(K_ROWS, sv_rows_kernel<DT, VEC, GR, MODE>, dim3((unsigned)(nrow * p.nsplit)), 0, p, h->w, gj[g],
+                   gn[g]);
         if (FUSED_LAST && g + 1 == ng) break;
-        mark(K_DECIDE, 0);
-        hipLaunchKernelGGL((sv_decide_kernel<DT, GR, MODE & MODE_ONEHOT>), dim3(B), dim3(kThreads), 0, s, p, h->w,
-                           gj[g], gn[g]);
-        mark(K_DECIDE, 1);
+        launch(K_DECIDE, sv_decide_kernel<DT, GR, MODE & MODE_ONEHOT>, dim3(B), 0, p, h->w, gj[g], gn[g]);
     }
-    mark(K_RESID, 0);
     if constexpr (FUSED_LAST) // (one-hot drafts: the final draw forms p without x itself)
-        hipLaunchKernelGGL((sv_resid_kernel<DT, VEC, MODE>), dim3(B * (unsigned)p.nsplit * kParts), dim3(kThreads), 0,
-                           s, p, h->w, gj[ng - 1], gn[ng - 1]);
-    mark(K_RESID, 1);
-    mark(K_DRAW, 0);
-    hipLaunchKernelGGL((sv_draw_kernel<DT, VEC, MODE>), dim3(B), dim3(kThreads),
-                       (size_t)p.nsplit * Seg<DT>::SEGS * sizeof(double), s, p, h->w, FUSED_LAST ? h->w.fin : h->w.st);
-    mark(K_DRAW, 1);
+        launch(K_RESID, sv_resid_kernel<DT, VEC, MODE>, dim3(B * (unsigned)p.nsplit * kParts), 0, p, h->w, gj[ng - 1],
+               gn[ng - 1]);
+    launch(K_DRAW, sv_draw_kernel<DT, VEC, MODE>, dim3(B), (uint32_t)(p.nsplit * Seg<DT>::SEGS * sizeof(double)), p,
+           h->w, (const SeqState*)(FUSED_LAST ? h->w.fin : h->w.st));
 }
 
 size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -2193,20 +2206,11 @@ int spec_verify_run(spec_verify_t* h, const spec_verify_args* a, void* hip_strea
     p.status_out = a->device_status;
 
     const bool timing = h->ev && h->timing_n < h->timing_max;
-    int slot = 0;
-    auto mark = [&](int k, int which) {
-        if (!timing || slot >= kMaxSlots) return;
-        const int idx = h->timing_n * kMaxSlots + slot;
-        (void)hipEventRecord(h->ev[idx * 2 + which], s);
-        if (which == 1) {
-            h->ev_kernel[idx] = k;
-            ++slot;
-        }
-    };
+    StepLauncher launch{h, s, timing, 0};
     const int bf = h->cfg.dtype == SV_BF16;
     const int mode = (p.onehot ? MODE_ONEHOT : 0) | (p.toff ? MODE_PACKED : 0);
     // runtime choices -> kernel variants (greedy steps never take the one-hot variant)
-#define SV_STEP(DT, VEC, GR, M) enqueue_step<DT, VEC, GR, M>(h, p, s, mark)
+#define SV_STEP(DT, VEC, GR, M) enqueue_step<DT, VEC, GR, M>(h, p, s, launch)
 #define SV_STEP_M(DT, VEC, GR) do { switch (GR ? (mode & MODE_PACKED) : mode) { \
         case 0: SV_STEP(DT, VEC, GR, 0); break; case 1: SV_STEP(DT, VEC, GR, 1); break; \
         case 2: SV_STEP(DT, VEC, GR, 2); break; default: SV_STEP(DT, VEC, GR, 3); break; } } while (0)

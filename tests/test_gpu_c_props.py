@@ -36,6 +36,41 @@ def test_bitwise_determinism():
                 assert np.array_equal(v.view(np.uint8), outs[0][k].view(np.uint8)), k
 
 
+@pytest.mark.parametrize("name,derived", [("zipf64", False), ("greedy1024", False), ("sched256", True)])
+def test_timed_runs_match_untimed_runs(name, derived):
+    # per-kernel timing launches every kernel with events attached to the
+    # dispatch; the outputs must not change, and every kernel of the step must
+    # report a positive time (the residual pass only where it runs)
+    D = _D()
+    w = synth.WORKLOADS[name].with_(B=24)
+    if derived:
+        w = w.with_(tau_choices=(0.0,))
+    prob = synth.make_problem(w)
+    print(f"[case] timed runs {name} B24", flush=True)
+    dp = D.from_problem(prob)
+    sv = D.handle_for(dp)
+    sv.run(dp.args())
+    ref = dp.fetch()
+    sv.timing_begin(3)
+    for _ in range(3):
+        sv.run(dp.args())
+    timed = dp.fetch()
+    ms, runs = sv.timing_end()
+    sv.close()
+    assert runs == 3
+    for k, v in ref.items():
+        if v is not None:
+            assert np.array_equal(v.view(np.uint8), timed[k].view(np.uint8)), k
+    greedy = w.temperature == 0
+    for k in ("sv_plan", "sv_rows", "sv_decide", "sv_draw"):
+        assert ms[k] > 0.0, (k, ms)
+    assert (ms["sv_resid"] > 0.0) == (not greedy), ms
+    orc = O.verify_problem(prob, all_rows=True)
+    rep = PU.compare(f"timed {name}", timed, orc, dtype=w.dtype, greedy=greedy, derived=derived)
+    print(rep.line(), flush=True)
+    assert not rep.mismatches, rep.mismatches[:5]
+
+
 @pytest.mark.parametrize("name", ["zipf64", "peaked512"])
 def test_batch_invariance(name):
     D = _D()
