@@ -179,8 +179,10 @@ int spec_verify_destroy(spec_verify_t* h);
 const char* spec_verify_status_string(int status);
 
 /* Per-kernel timing with HIP events, for benchmarks.  After
- * spec_verify_timing_begin(h, max_calls), the next max_calls runs record an
- * event before and after each kernel on the run's stream.
+ * spec_verify_timing_begin(h, max_calls), the next max_calls runs launch each
+ * kernel with a start and a stop event attached to its dispatch
+ * (hipExtLaunchKernelGGL), which time the kernel's execution itself; a kernel
+ * the step does not launch records nothing.  Outputs are unchanged.
  * spec_verify_timing_end synchronises those events, writes the summed
  * milliseconds of kernel k to ms[k] (k < n_kernels, see
  * spec_verify_kernel_name), the number of timed runs to *n_runs, and frees
