@@ -1,5 +1,6 @@
-"""GPU parity of long draft blocks, where the last position group deals several
-rows to each workgroup (four or more position groups: K >= 11).
+"""GPU parity of long draft blocks, whose last position group (four or more
+groups: K >= 11) is streamed from a list of its needed rows, or, above 4096
+sequences, with several rows dealt to each workgroup.
 
 Acceptance is made high (draft = target + small noise, or a greedy drafter
 that matches often) so that many sequences reach the last group, and low in
@@ -89,6 +90,18 @@ def test_one_hot():
     w = BASE.with_(B=19, K=18, V=12000, draft_mode=1, token_mode=2, target_kind=1, zipf_s=1.3,
                    zipf_jitter=0.3, sigma_first=0.2, sigma_last=0.2, temperature=0.7, seed=160)
     _run("late one-hot", w)
+
+
+@pytest.mark.parametrize("greedy", [False, True])
+def test_batch_above_the_row_list_limit(greedy):
+    # more than 4096 sequences: the last group's rows go through the
+    # eight-rows-per-workgroup kernel instead of the row list
+    if greedy:
+        w = synth.WORKLOADS["greedy1024"].with_(B=4101, K=12, V=520, p_match=0.97, seed=175)
+    else:
+        w = BASE.with_(B=4101, K=12, V=520, sigma_first=0.01, sigma_last=0.01, seed=176)
+    res, _ = _run(f"late B=4101 greedy={greedy}", w)
+    assert (res["accepted_len"] >= _last_group_start(w.K) - 1).sum() >= 50
 
 
 def test_packed_ragged_lengths():
