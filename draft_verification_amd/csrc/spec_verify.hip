@@ -74,14 +74,14 @@ constexpr int kPerLane = kSplit / kThreads;       // 64 elements per lane per sp
 constexpr int kMaxGroup = 16;                     // positions per group
 constexpr int kMaxGroups = 64;                    // groups per step (K + 1 <= 2 + 2 + 4 + 8 + 16 * 59)
 
-enum { CTL_STATUS = 0, CTL_SCHED_STATUS = 1, CTL_CONF_STATUS = 2, CTL_ROWS_N = 3, CTL_WORDS = 64 };
+enum { CTL_STATUS = 0, CTL_SCHED_STATUS = 1, CTL_CONF_STATUS = 2, CTL_WORDS = 64 };
 enum { FL_ACC = 1, FL_LEN = 2 };
 // Compile-time variants of the step kernels: MODE_ONEHOT (q is the point mass
 // at the drafted token; never with greedy verification) and MODE_PACKED (rows
 // addressed through per-sequence offsets).
 enum { MODE_ONEHOT = 1, MODE_PACKED = 2 };
 enum { KIND_NONE = -1, KIND_RESID = 0, KIND_BONUS = 1, KIND_GREEDY = 2, KIND_BAD = 3 };
-enum { K_PLAN = 0, K_ROWS = 1, K_DECIDE = 2, K_RESID = 3, K_DRAW = 4, K_LIST = 5, K_COUNT = 6 };
+enum { K_PLAN = 0, K_ROWS = 1, K_DECIDE = 2, K_RESID = 3, K_DRAW = 4, K_COUNT = 5 };
 
 struct SeqState {
     double S;      // survival product S_j of the positions evaluated so far
@@ -106,7 +106,6 @@ struct Work {
     SeqState* st;     // [max_batch]
     SeqState* fin;    // [max_batch] state after the last group, stored by sv_resid (which takes its decisions)
     int* live;        // [max_batch] (L + 1) << 2 | flags, the part of st that sv_rows reads
-    int* rowlist;     // [max_batch * 2 * kMaxGroup] a group's needed rows, (b << 5) | ((j - j0) << 1) | draft
     double* seg;      // [max_batch][nsplit][64] residual mass per segment of a split
     float* xlog;      // [max_batch][2K+1] logit of the drafted token in each row
 };
@@ -766,8 +765,7 @@ __global__ __launch_bounds__(kThreads, (DT == SV_BF16 && VEC) ? 8 : 1) void sv_r
     rows_finish<DT, GREEDY>(p, w, c, r, redf, redd, redi, t);
 }
 
-// The same statistics for the last position group from the fourth group on
-// when the batch is too large for the row list (sv_compact, sv_rows_list),
+// The same statistics for the last position group from the fourth group on,
 // where the walks of most sequences have ended (typically a few in a hundred
 // are still open) and one workgroup per row would mostly start only to find
 // its row unneeded.  The group's rows (sequence, row slot) are dealt to nw =
@@ -818,106 +816,6 @@ __global__ __launch_bounds__(kThreads, (DT == SV_BF16 && VEC) ? 8 : 1) void sv_r
             const int b = i / slots, slot = i % slots;
             const bool draft = !GREEDY && slot >= G;
             const int j = j0 + (draft ? slot - G : slot);
-            int z = 0;
-            asm volatile("" : "+v"(z)); // opaque: the index below is computed afresh in this copy
-            const int tl = (wv << 6) | (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, (unsigned)z));
-            const RowRef r = row_ref<DT, PK>(p, b, j, draft, split);
-            Chunk<DT> c;
-            c.template issue<VEC>(r.row, split * kSplit, p.V, tl);
-            c.template fix_tail<VEC>(split * kSplit, p.V, tl);
-            rows_finish<DT, GREEDY>(p, w, c, r, redf, redd, redi, tl);
-        }
-    }
-}
-
-// Needed rows of one sequence in a position group: target rows j0 .. j0+nt-1
-// and draft rows j0 .. j0+nd-1 (each rule needs a prefix of the positions).
-__device__ __forceinline__ void group_need(int lv, int j0, int G, int K, bool target_only, int& nt, int& nd)
-{
-    const int flags = lv & 3, L = (lv >> 2) - 1;
-    const int j1 = j0 + G - 1;
-    int tend = min(j1, K + 1);
-    if (L >= 0) tend = min(tend, L + 1);
-    nt = (flags & FL_ACC) ? max(tend - j0 + 1, 0) : 0;
-    int dend = min(j1, K);
-    if (!(flags & FL_LEN)) dend = (flags & FL_ACC) ? min(dend, L) : j0 - 1;
-    nd = target_only ? 0 : max(dend - j0 + 1, 0);
-}
-
-// The needed rows of a position group as a list (one workgroup, sequences in
-// order, inside a sequence target rows then draft rows) and their count in
-// ctl[CTL_ROWS_N], so that the group's row kernel deals them to its first
-// workgroups: a group where few sequences are still open then streams its
-// rows at once instead of interleaving them with workgroups that only find
-// their row unneeded.
-constexpr int kListMaxB = 4096; // larger batches: sv_rows_late
-
-template <bool TARGET_ONLY>
-__global__ __launch_bounds__(kThreads) void sv_compact_kernel(Params p, Work w, int j0, int G)
-{
-    __shared__ int s_wsum[kWaves];
-    const int t = (int)threadIdx.x, lane = t & 63;
-    int base = 0;
-    for (int c0 = 0; c0 < p.B; c0 += kThreads) {
-        const int b = c0 + t;
-        int nt = 0, nd = 0;
-        if (b < p.B) group_need(w.live[b], j0, G, p.K, TARGET_ONLY, nt, nd);
-        const int cnt = nt + nd;
-        int incl = cnt;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const int n = __shfl_up(incl, o);
-            if (lane >= o) incl += n;
-        }
-        if (lane == 63) s_wsum[t >> 6] = incl;
-        __syncthreads();
-        int pre = base + incl - cnt, total = 0;
-#pragma unroll
-        for (int v = 0; v < kWaves; ++v) {
-            if (v < (t >> 6)) pre += s_wsum[v];
-            total += s_wsum[v];
-        }
-        for (int r = 0; r < nt; ++r) w.rowlist[pre + r] = (b << 5) | (r << 1);
-        for (int r = 0; r < nd; ++r) w.rowlist[pre + nt + r] = (b << 5) | (r << 1) | 1;
-        base += total;
-        __syncthreads(); // (s_wsum is reused by the next chunk)
-    }
-    if (t == 0) w.ctl[CTL_ROWS_N] = base;
-}
-
-// Row statistics over a group's row list: task i is split i % nsplit of
-// listed row i / nsplit.  Workgroup w takes tasks w, w + nw, ... (kRowsLate of
-// them, each in its own straight-line copy of the row code, as in
-// sv_rows_late); tasks past the list's end exit after reading its length.
-// Used for the last group from the fourth on: with its rows listed, the few
-// needed rows go to the first workgroups of the launch (1.7 us per step less
-// than sv_rows_late at B = 256, K = 16).  On the third group (a quarter of the
-// sequences open) listing cost 1.5 us, and 3 us from the second group on: the
-// extra launch outweighs the gain there.
-template <int DT, bool VEC, bool GREEDY, int MODE>
-__global__ __launch_bounds__(kThreads, (DT == SV_BF16 && VEC) ? 8 : 1) void sv_rows_list_kernel(Params p, Work w,
-                                                                                                int j0)
-{
-    constexpr bool PK = (MODE & MODE_PACKED) != 0;
-    __shared__ float redf[kWaves];
-    __shared__ double redd[kWaves];
-    __shared__ int redi[kWaves];
-    typedef const __attribute__((address_space(4))) int* cptr;
-    const unsigned ns = (unsigned)p.nsplit;
-    const unsigned nw = gridDim.x;
-    const int n = ((cptr)w.ctl)[CTL_ROWS_N];
-    const int wv = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
-#pragma unroll
-    for (int k = 0; k < kRowsLate; ++k) {
-        __builtin_amdgcn_sched_barrier(0);
-        const unsigned task = blockIdx.x + (unsigned)k * nw;
-        const int q = (int)(task / ns);
-        if (q < n) {
-            const int code = ((cptr)w.rowlist)[q];
-            const int split = (int)(task % ns);
-            const int b = code >> 5;
-            const bool draft = (code & 1) != 0;
-            const int j = j0 + ((code >> 1) & 15);
             int z = 0;
             asm volatile("" : "+v"(z)); // opaque: the index below is computed afresh in this copy
             const int tl = (wv << 6) | (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, (unsigned)z));
@@ -1835,7 +1733,7 @@ __global__ void sv_conf_status_kernel(ConfParams q, AuxWork w)
 // ---------------------------------------------------------------- host side
 
 
-const char* const kKernelNames[K_COUNT] = {"sv_plan", "sv_rows", "sv_decide", "sv_resid", "sv_draw", "sv_compact"};
+const char* const kKernelNames[K_COUNT] = {"sv_plan", "sv_rows", "sv_decide", "sv_resid", "sv_draw"};
 constexpr int kMaxSlots = 64; // timed launches per run
 
 } // namespace
@@ -1909,12 +1807,7 @@ void enqueue_step(const spec_verify* h, const Params& p, hipStream_t s, Launch& 
     constexpr bool FUSED_LAST = !GR && !OH;
     for (int g = 0; g < ng; ++g) {
         const long long nrow = (long long)B * slots(g);
-        if (VEC && g >= 3 && g + 1 == ng && p.B <= kListMaxB) {
-            // the last group: its needed rows listed first, then streamed from the list
-            launch(K_LIST, sv_compact_kernel<GR || OH>, dim3(1), 0, p, h->w, gj[g], gn[g]);
-            launch(K_ROWS, sv_rows_list_kernel<DT, true, GR, MODE>,
-                   dim3((unsigned)((nrow * p.nsplit + kRowsLate - 1) / kRowsLate)), 0, p, h->w, gj[g]);
-        } else if (VEC && g >= 3 && g + 1 == ng) // (the unaligned path keeps one row per workgroup)
+        if (VEC && g >= 3 && g + 1 == ng) // (the unaligned path keeps one row per workgroup)
             launch(K_ROWS, sv_rows_late_kernel<DT, true, GR, MODE>,
                    dim3((unsigned)((nrow + kRowsLate - 1) / kRowsLate * p.nsplit)), 0, p, h->w, gj[g], gn[g]);
         else
@@ -2061,7 +1954,6 @@ int spec_verify_create(const spec_verify_config* cfg, spec_verify_t** out)
     const size_t o_st = off; off = align_up(off + (size_t)cfg->max_batch * sizeof(SeqState));
     const size_t o_fi = off; off = align_up(off + (size_t)cfg->max_batch * sizeof(SeqState));
     const size_t o_lv = off; off = align_up(off + (size_t)cfg->max_batch * sizeof(int));
-    const size_t o_rl = off; off = align_up(off + (size_t)cfg->max_batch * 2 * kMaxGroup * sizeof(int));
     const size_t o_sg = off; off = align_up(off + (size_t)cfg->max_batch * ns * kSegStride * sizeof(double));
     const size_t o_xl = off; off = align_up(off + nrow * sizeof(float));
     const long long ncand = std::min((long long)cfg->max_batch * cfg->max_draft, (long long)SV_MAX_SCHED_CANDIDATES);
@@ -2082,7 +1974,6 @@ int spec_verify_create(const spec_verify_config* cfg, spec_verify_t** out)
     h->w.st = (SeqState*)(base + o_st);
     h->w.fin = (SeqState*)(base + o_fi);
     h->w.live = (int*)(base + o_lv);
-    h->w.rowlist = (int*)(base + o_rl);
     h->w.seg = (double*)(base + o_sg);
     h->w.xlog = (float*)(base + o_xl);
     h->aux.ctl = h->w.ctl;

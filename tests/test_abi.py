@@ -44,7 +44,7 @@ def test_status_strings_and_kernel_names(B):
     assert "invalid" in B.status_string(B.SV_EINVAL)
     assert B.status_string(12345) == "unknown status"
     names = B.kernel_names()
-    assert names == ["sv_plan", "sv_rows", "sv_decide", "sv_resid", "sv_draw", "sv_compact"]
+    assert names == ["sv_plan", "sv_rows", "sv_decide", "sv_resid", "sv_draw"]
     assert B.lib().spec_verify_kernel_name(99) == b""
 
 

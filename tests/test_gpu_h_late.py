@@ -1,6 +1,5 @@
-"""GPU parity of long draft blocks, whose last position group (four or more
-groups: K >= 11) is streamed from a list of its needed rows, or, above 4096
-sequences, with several rows dealt to each workgroup.
+"""GPU parity of long draft blocks, where the last position group deals several
+rows to each workgroup (four or more position groups: K >= 11).
 
 Acceptance is made high (draft = target + small noise, or a greedy drafter
 that matches often) so that many sequences reach the last group, and low in
@@ -93,9 +92,8 @@ def test_one_hot():
 
 
 @pytest.mark.parametrize("greedy", [False, True])
-def test_batch_above_the_row_list_limit(greedy):
-    # more than 4096 sequences: the last group's rows go through the
-    # eight-rows-per-workgroup kernel instead of the row list
+def test_large_batch(greedy):
+    # 4101 sequences: many workgroup columns, several open sequences sharing one
     if greedy:
         w = synth.WORKLOADS["greedy1024"].with_(B=4101, K=12, V=520, p_match=0.97, seed=175)
     else:
