@@ -141,6 +141,63 @@ def timed_inputs_check(probs, outs):
                     "lengths and prefix equal and the final token is one of the two across the step"}
 
 
+# inputs and GPU outputs of the later legs, for the oracle in the CPU-baseline leg
+LEG_DATA = {}
+
+
+def _timed(fn, seconds):
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        r = fn()
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or reps >= 1000:
+            return r, el / reps
+
+
+def next_rows_oracle(synth, seconds=2.0):
+    """The oracle on each later leg's inputs (the one-hot and packed verify
+    steps, the admission decision, the calibrated confidences): its time per
+    call on the host, and whether the GPU's outputs match it."""
+    from oracle import oracle as O
+    threads = len(os.sched_getaffinity(0))
+    res = {}
+    if "onehot" in LEG_DATA:
+        probs, outs = LEG_DATA["onehot"]
+        chk = timed_inputs_check(probs, outs)
+        _, sec = _timed(lambda: O.verify_problem(probs[0], threads=threads), seconds)
+        L = int(outs[0]["verify_len_out"].sum())
+        res["onehot"] = {"value": L / sec, "unit": "verified draft positions/s", "s_per_step": sec,
+                         "cores": threads, "vs_gpu": chk}
+    if "packed" in LEG_DATA:
+        L, outs = LEG_DATA["packed"]
+        probs = []
+        for s in (0, 1000):
+            prob = synth.make_problem(workload().with_(length_mode=0, tau_choices=(), seed=3 + s))
+            prob.verify_len = L.astype(np.int32)
+            probs.append(prob)
+        chk = timed_inputs_check(probs, outs)
+        _, sec = _timed(lambda: O.verify_problem(probs[0], threads=threads), seconds)
+        res["packed"] = {"value": float(L.sum()) / sec, "unit": "verified draft positions/s", "s_per_step": sec,
+                         "cores": threads, "vs_gpu": chk}
+    if "admission" in LEG_DATA:
+        conf, speed, vl, adm = LEG_DATA["admission"]
+        r, sec = _timed(lambda: O.schedule(conf, speed), seconds)
+        res["admission"] = {"us_per_call": sec * 1e6, "cores": 1, "margin": bool(r.margin),
+                            "vs_gpu": {"verify_len_equal": bool(np.array_equal(r.verify_len, vl)),
+                                       "admitted_equal": int(r.admitted) == adm}}
+    if "confidence" in LEG_DATA:
+        z, T, got = LEG_DATA["confidence"]
+        steps = [z.astype(np.float32)] * 3
+        r, sec = _timed(lambda: O.calibrated_confidence_steps(steps, T, delay=2, c_default=0.0), seconds)
+        _, handed, _ = r
+        want = np.asarray(handed[-1], np.float32)  # the third call hands over the first call's value
+        ulp = np.abs(got.view(np.int32).astype(np.int64) - want.view(np.int32).astype(np.int64))
+        res["confidence"] = {"us_per_call": sec * 1e6 / 3, "cores": 1,
+                             "vs_gpu": {"max_ulp": int(ulp.max()), "within_1_ulp": bool(ulp.max() <= 1)}}
+    return res
+
+
 def cpu_single_thread(seconds=2.0):
     """The oracle on one host thread for the two small workloads (tiny: B=4
     K=4 V=1024 fp32; zipf64: B=64 K=8 V=129280 bf16), about `seconds` each."""
@@ -195,10 +252,14 @@ def time_onehot(torch, B, D, synth, steps, warmup):
     rows_ms = kms["sv_rows"] / max(nruns, 1)
     bytes_step = sum(step_bytes(o, w)["bytes"] for o in outs) / 2.0
     positions = sum(int(o["verify_len_out"].sum()) for o in outs) / 2.0
+    gbps = bytes_step / (rows_ms / 1e3) / 1e9
+    LEG_DATA["onehot"] = (probs, outs)
     return {"value": positions / (ms / 1e3), "unit": "verified draft positions/s", "ms_per_step": ms,
             "mean_accepted": float(np.mean([o["accepted_len"].mean() for o in outs])),
-            "sv_rows_gbps": bytes_step / (rows_ms / 1e3) / 1e9, "rows_per_step": sum(
-                int(o["rows_read"].sum()) for o in outs) / 2.0,
+            "sv_rows_gbps": gbps, "rows_per_step": sum(int(o["rows_read"].sum()) for o in outs) / 2.0,
+            "roofline": {"bound": "hbm", "achieved": gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                         "frac": gbps / PEAK_HBM_GBPS, "kernel": "sv_rows", "kernel_avg_ms": rows_ms,
+                         "algorithmic_bytes_per_launch": bytes_step, "traffic": None},
             "kernel_avg_ms": {k: v / max(nruns, 1) for k, v in kms.items()},
             "workload": "one-hot drafts (greedy drafter) on peaked rows: B=256 K=16 V=129280 bf16, "
                         "Zipf(1.3)+N(0,0.3) at T=0.7, draft noise 0.2, L=16; target rows only"}
@@ -244,8 +305,23 @@ def time_packed(torch, B, D, synth, steps, warmup):
             del prob
         ms = _time_runs(torch, sv, [d.args() for d in dps], steps, warmup)
         outs = [d.fetch() for d in dps]
+        sv.timing_begin(steps)
+        stream = torch.cuda.current_stream().cuda_stream
+        for i in range(steps):
+            sv.run(dps[i % 2].args(), stream)
+        torch.cuda.synchronize()
+        kms, nruns = sv.timing_end()
+        rows_ms = kms["sv_rows"] / max(nruns, 1)
+        bytes_step = sum(step_bytes(o, base)["bytes"] for o in outs) / 2.0
+        gbps = bytes_step / (rows_ms / 1e3) / 1e9
+        if layout == "packed":
+            LEG_DATA["packed"] = (L.copy(), outs)
         out[layout] = {"ms_per_step": ms, "value": float(L.sum()) / (ms / 1e3),
                        "rows_per_step": sum(int(o["rows_read"].sum()) for o in outs) / 2.0,
+                       "roofline": {"bound": "hbm", "achieved": gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                                    "frac": gbps / PEAK_HBM_GBPS, "kernel": "sv_rows", "kernel_avg_ms": rows_ms,
+                                    "algorithmic_bytes_per_launch": bytes_step, "traffic": None},
+                       "kernel_avg_ms": {k: v / max(nruns, 1) for k, v in kms.items()},
                        "logit_bytes_held": sum(int(d.target.numel() * d.target.element_size()) + (
                            int(d.draft.numel() * d.draft.element_size()) if d.draft is not None else 0)
                            for d in dps) / 2.0}
@@ -276,6 +352,7 @@ def time_confidence(sv, torch, B, synth, Bn, K, steps, warmup):
         sv.confidence(a, stream)
     e1.record()
     torch.cuda.synchronize()
+    LEG_DATA["confidence"] = (z.cpu().numpy(), T.cpu().numpy(), out.cpu().numpy())
     return {"us_per_call": e0.elapsed_time(e1) / steps * 1e3, "B": Bn, "K": K, "delay": 2,
             "inputs": "logits uniform in [-2, 2) (Philox key 600), temperatures 0.8 .. 1.6"}
 
@@ -300,6 +377,7 @@ def time_admission(sv, torch, B, synth, Bn, K, steps, warmup):
         sv.schedule(a, stream)
     e1.record()
     torch.cuda.synchronize()
+    LEG_DATA["admission"] = (conf, speed, vl.cpu().numpy(), int(adm.item()))
     return {"us_per_call": e0.elapsed_time(e1) / steps * 1e3, "B": Bn, "K": K, "candidates": Bn * K,
             "admitted": int(adm.item()),
             "inputs": "confidences uniform in [0.3, 1) (Philox key 500), step time 20 + 0.05 n"}
@@ -465,6 +543,7 @@ def main():
         out["cpu_baseline"] = cpu_baseline(probs[0], L_total[0])
         out["cpu_baseline"]["single_thread"] = cpu_single_thread()
         out["cpu_baseline"]["timed_inputs_vs_oracle"] = timed_inputs_check(probs, outs)
+        out["cpu_baseline"]["next_rows"] = next_rows_oracle(synth)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
