@@ -30,9 +30,15 @@
 // launch a pure stream: an agent-scope fence costs ~130 ns, serialised, on
 // this chip, so work is never handed between workgroups inside a launch.
 //
+// When the step samples with draft probabilities, the last group has no
+// sv_decide launch: sv_resid takes those decisions at its start.
+//
 // After the last group:
-//   sv_resid   per (rejecting sequence, split, half split): segment sums of
-//              max(0, p - q) over the rejected row pair.
+//   sv_resid   per (sequence, split, half split): the last group's decisions
+//              (every workgroup of a sequence derives them; one writes them),
+//              then for a rejecting sequence the segment sums of
+//              max(0, p - q) over the rejected row pair.  (One-hot drafts have
+//              no residual pass: sv_draw forms p without x itself.)
 //   sv_draw    per sequence: inverse-CDF draw (replacement or bonus) by split
 //              and segment prefix in fp64, then one segment's tokens scanned
 //              in token order; writes the outputs.
@@ -1776,7 +1782,8 @@ struct StepLauncher {
 };
 
 // One verification step on stream s: plan, then per position group the row
-// statistics and the decisions, then the residual masses and the final draw.
+// statistics and the decisions (those of the last group inside the residual
+// pass when there is one), then the residual masses and the final draw.
 // Groups hold 3, 3, 4, 8, 16, 16, ... positions (a remainder of one position
 // joins the previous group).  Early groups are small because most sequences
 // stop early; each group costs a fixed few microseconds (the launches' ramp and
