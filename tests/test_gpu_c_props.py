@@ -71,6 +71,37 @@ def test_timed_runs_match_untimed_runs(name, derived):
     assert not rep.mismatches, rep.mismatches[:5]
 
 
+def test_two_handles_on_two_streams():
+    # separate handles are independent: two steps enqueued on two streams at
+    # once give the same outputs as each run alone on the default stream
+    D = _D()
+    probs = [synth.make_problem(synth.WORKLOADS["zipf64"].with_(B=48, seed=71)),
+             synth.make_problem(synth.WORKLOADS["peaked512"].with_(B=40, K=12, V=30000, seed=72))]
+    print("[case] two handles on two streams", flush=True)
+    dps = [D.from_problem(p) for p in probs]
+    hs = [D.handle_for(dp) for dp in dps]
+    alone = []
+    for h, dp in zip(hs, dps):
+        h.run(dp.args())
+        alone.append(dp.fetch())
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    ev = torch.cuda.Event()
+    ev.record()
+    for st in streams:
+        st.wait_event(ev)
+    for rep in range(3):
+        for h, dp, st in zip(hs, dps, streams):
+            h.run(dp.args(), st.cuda_stream)
+    torch.cuda.synchronize()
+    for dp, ref in zip(dps, alone):
+        got = dp.fetch()
+        for k, v in ref.items():
+            if v is not None:
+                assert np.array_equal(v.view(np.uint8), got[k].view(np.uint8)), k
+    for h in hs:
+        h.close()
+
+
 @pytest.mark.parametrize("name", ["zipf64", "peaked512"])
 def test_batch_invariance(name):
     D = _D()
