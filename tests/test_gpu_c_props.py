@@ -84,6 +84,7 @@ def test_two_handles_on_two_streams():
     for h, dp in zip(hs, dps):
         h.run(dp.args())
         alone.append(dp.fetch())
+        dp.alloc_outputs(True, "cuda:0")  # fresh output buffers (sentinels) for the concurrent runs
     streams = [torch.cuda.Stream(), torch.cuda.Stream()]
     ev = torch.cuda.Event()
     ev.record()
