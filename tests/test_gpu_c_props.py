@@ -103,6 +103,43 @@ def test_two_handles_on_two_streams():
         h.close()
 
 
+@pytest.mark.parametrize("name", ["zipf64", "greedy1024"])
+def test_graph_capture_replays(name):
+    # a step is only kernel launches on the caller's stream, so it can be
+    # captured in a HIP graph; every replay, with eager work and
+    # synchronisations between replays, must give the eager outputs
+    D = _D()
+    prob = synth.make_problem(synth.WORKLOADS[name].with_(B=32, seed=73))
+    print(f"[case] graph capture {name}", flush=True)
+    dp = D.from_problem(prob)
+    sv = D.handle_for(dp)
+    sv.run(dp.args())
+    ref = dp.fetch()
+    dp.alloc_outputs(True, "cuda:0")
+    args = dp.args()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        sv.run(args)  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        sv.run(args)
+    for rep in range(4):
+        for t in (dp.accepted_len, dp.out_tokens, dp.verify_len_out):
+            t.fill_(-9)  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = dp.fetch()
+        for k, v in ref.items():
+            if v is not None:
+                assert np.array_equal(v.view(np.uint8), got[k].view(np.uint8)), (rep, k)
+    del g
+    sv.close()
+
+
 @pytest.mark.parametrize("name", ["zipf64", "peaked512"])
 def test_batch_invariance(name):
     D = _D()
