@@ -265,6 +265,37 @@ def time_onehot(torch, B, D, synth, steps, warmup):
                         "Zipf(1.3)+N(0,0.3) at T=0.7, draft noise 0.2, L=16; target rows only"}
 
 
+def time_graph_replay(torch, sv, argv, steps):
+    """Time per step when each input set's step is captured once in a HIP graph
+    and replayed (no host launch cost per kernel): a step is only kernel
+    launches on the caller's stream, so a serving loop can capture it."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for a in argv:
+            sv.run(a)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graphs = []
+    for a in argv:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            sv.run(a)
+        graphs.append(g)
+    for i in range(4):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        graphs[i % len(graphs)].replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    del graphs
+    return ms
+
+
 def _time_runs(torch, sv, argv, steps, warmup):
     stream = torch.cuda.current_stream().cuda_stream
     for i in range(warmup):
@@ -469,6 +500,9 @@ def main():
                  "p90": float(np.percentile(per_step, 90)), "n": int(args.steps), "unit": "ms",
                  "method": "HIP events between consecutive steps on the launch stream (a separate pass)"}
 
+    # the same steps replayed from HIP graphs (one captured step per input set)
+    graph_ms = time_graph_replay(torch, sv, argv, args.steps)
+
     # per-kernel timing (HIP events around each launch, same stream)
     sv.timing_begin(args.steps)
     for i in range(args.steps):
@@ -522,6 +556,7 @@ def main():
                      "traffic_source": "rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated, bytes per step; null "
                                        "when the kernel source changed since the counters were taken"},
         "step_ms_distribution": step_dist,
+        "graph_replay_ms_per_step": graph_ms,
         "copy_ceiling": {"gbps_rw": ceiling["gbps_rw"], "bytes": 2 * ceiling["copy_bytes_read"],
                          "what": "torch device copy of 1 GiB, (read + write bytes) / time; sv_rows only reads"},
         "step_hbm_gbps": bytes_step / (ms_step / 1e3) / 1e9,

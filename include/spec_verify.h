@@ -169,7 +169,10 @@ int spec_verify_create(const spec_verify_config* cfg, spec_verify_t** out);
  * device state.  Returns SV_OK, SV_EINVAL or SV_EUNSUPPORTED. */
 int spec_verify_check(const spec_verify_config* cfg, const spec_verify_args* a);
 
-/* Enqueue one verification step on hip_stream (a hipStream_t, or NULL). */
+/* Enqueue one verification step on hip_stream (a hipStream_t, or NULL).  The
+ * step is kernel launches on that stream only (no allocation, copy, memset or
+ * synchronisation), so it may be captured in a HIP graph; a captured step
+ * reads the pointers and sizes of the args it was captured with. */
 int spec_verify_run(spec_verify_t* h, const spec_verify_args* a, void* hip_stream);
 
 /* Free the handle.  The caller synchronises the stream first.  NULL is a no-op. */
