@@ -126,6 +126,21 @@ def test_tau_derived_confidence(taus):
     _run_case(f"tau derived {taus}", w, derived=True)
 
 
+@pytest.mark.parametrize("given", [False, True])
+def test_tau_special_values(given):
+    # tau NaN, +inf, 1.0 (above every survival below 1) verify nothing; -inf
+    # and -0.0 verify every position (reading R8)
+    w = synth.WORKLOADS["peaked512"].with_(B=10, K=6, V=3000, tau_choices=(0.3,), seed=92)
+    prob = synth.make_problem(w)
+    prob.tau = np.array([np.nan, np.inf, -np.inf, -0.0, 1.0, 0.0, np.nan, 2.0, -1.0, 1e-30], np.float32)
+    if given:
+        prob.confidence = np.full((w.B, w.K), 0.9, np.float32)
+    res, orc, _ = _run_case(f"tau special given={given}", w, prob=prob, derived=not given)
+    L = res["verify_len_out"]
+    assert L[0] == 0 and L[1] == 0 and L[4] == 0 and L[6] == 0 and L[7] == 0
+    assert L[2] == w.K and L[3] == w.K and L[5] == w.K and L[8] == w.K
+
+
 def test_tau_derived_greedy_rejected():
     D = _dev()
     from draft_verification_amd import binding as B
