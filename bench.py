@@ -450,7 +450,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this benchmark runs on exactly one GPU; --gpus {args.gpus} is not supported "
-              "(the verification step has no cross-GPU part; see the design notes on sharding).",
+              "(sequences are independent, so a batch would shard across GPUs with no exchange; this run has one GPU).",
               file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:

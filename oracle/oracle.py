@@ -228,7 +228,7 @@ def calibrated_confidence_steps(logits_steps, temperature, delay: int, c_default
     causal barrier between the decision and the tokens); zhichai.net article,
     section "Under the hood": Sequential Temperature Scaling.
 
-    Reading (listed in the design notes): at each step the calibrated
+    Reading where the pages leave it open: at each step the calibrated
     confidence of position j is sigmoid(z_j / T_j), in fp64, rounded to fp32
     (a temperature that is not finite and positive gives 0 and flags bad
     input); the value handed to the length decision is the calibrated value

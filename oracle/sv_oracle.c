@@ -31,7 +31,7 @@
  *       user nothing"; zhichai.net, section "Under the hood".)  The rule used
  *    here: S_0 = 1, S_j = S_{j-1} c_j, L = max({0} U {j : S_j >= tau}).
  *
- * Readings where the pages are silent (each is listed in the design notes):
+ * Readings where the pages are silent (the GPU path takes the same ones):
  *  - K+1 target rows per sequence; row K+1 is the distribution of the bonus
  *    token after the whole block.
  *  - One temperature T for target and draft: p = softmax(l_t / T),
@@ -423,7 +423,7 @@ int svo_max_threads(void)
  * the hood": each request's verified prefix is chosen to maximise accepted
  * tokens times verification speed.
  *
- * Readings (listed in the design notes):
+ * Readings where the pages leave the scheduler open:
  *  - a candidate is drafted position j of sequence b, with survival
  *    S_bj = prod_{i<=j} c_bi (fp64, left to right);
  *  - confidences outside [0, 1] (NaN included) are clamped into it (NaN -> 0)
