@@ -74,8 +74,10 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_entry(src_hash: str):
-    """HBM bytes per launch from committed counter runs, if they match this source."""
+def traffic_entry(src_hash: str, leg: str = None):
+    """HBM bytes of a step's sv_rows launches from committed counter runs, if
+    they match this source: the main workload, or a later leg ("onehot",
+    "packed", "dense_same_lengths")."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
@@ -83,6 +85,8 @@ def traffic_entry(src_hash: str):
         return None
     if t.get("kernel_src_sha") != src_hash:
         return None
+    if leg is not None:
+        return t.get("legs", {}).get(leg, {}).get("hbm_bytes_per_launch")
     return t.get("hbm_bytes_per_launch")
 
 
@@ -259,7 +263,8 @@ def time_onehot(torch, B, D, synth, steps, warmup):
             "sv_rows_gbps": gbps, "rows_per_step": sum(int(o["rows_read"].sum()) for o in outs) / 2.0,
             "roofline": {"bound": "hbm", "achieved": gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                          "frac": gbps / PEAK_HBM_GBPS, "kernel": "sv_rows", "kernel_avg_ms": rows_ms,
-                         "algorithmic_bytes_per_launch": bytes_step, "traffic": None},
+                         "algorithmic_bytes_per_launch": bytes_step,
+                         "traffic": traffic_entry(kernel_source_hash(), "onehot")},
             "kernel_avg_ms": {k: v / max(nruns, 1) for k, v in kms.items()},
             "workload": "one-hot drafts (greedy drafter) on peaked rows: B=256 K=16 V=129280 bf16, "
                         "Zipf(1.3)+N(0,0.3) at T=0.7, draft noise 0.2, L=16; target rows only"}
@@ -351,7 +356,9 @@ def time_packed(torch, B, D, synth, steps, warmup):
                        "rows_per_step": sum(int(o["rows_read"].sum()) for o in outs) / 2.0,
                        "roofline": {"bound": "hbm", "achieved": gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                                     "frac": gbps / PEAK_HBM_GBPS, "kernel": "sv_rows", "kernel_avg_ms": rows_ms,
-                                    "algorithmic_bytes_per_launch": bytes_step, "traffic": None},
+                                    "algorithmic_bytes_per_launch": bytes_step,
+                                    "traffic": traffic_entry(kernel_source_hash(),
+                                                             "packed" if layout == "packed" else "dense_same_lengths")},
                        "kernel_avg_ms": {k: v / max(nruns, 1) for k, v in kms.items()},
                        "logit_bytes_held": sum(int(d.target.numel() * d.target.element_size()) + (
                            int(d.draft.numel() * d.draft.element_size()) if d.draft is not None else 0)
