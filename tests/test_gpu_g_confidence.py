@@ -118,13 +118,25 @@ def test_confidence_schedule_verify_chain():
     _, o_out, _ = O.calibrated_confidence_steps(z, T, 2, 0.0)
     g_conf = conf.cpu().numpy()
     assert _ulps(g_conf, o_out[-1]).max() <= 1
-    # each stage against its own definition on the same inputs: the admission
-    # oracle takes the confidences the device handed over
-    o_s = O.schedule(g_conf, speed)
+    # the oracle's own chain: its calibrated, delayed confidences feed its
+    # admission rule, whose lengths feed its verification; nothing is taken
+    # from the device.  The device's confidences may differ by one fp32 ulp,
+    # which can only change the admission where two ranked survivals at the
+    # stop are that close: then the admitted count must still agree.
+    o_conf = np.asarray(o_out[-1], np.float32)
+    o_s = O.schedule(o_conf, speed)
     assert not o_s.margin and o_s.admitted > 0
-    np.testing.assert_array_equal(vl.cpu().numpy(), o_s.verify_len)
+    g_L = vl.cpu().numpy()
+    S = np.sort(o_s.survival.reshape(-1))[::-1]
+    m = o_s.admitted
+    boundary_tie = 0 < m < S.size and abs(S[m - 1] - S[m]) <= 4 * np.spacing(np.float32(S[m - 1]))
+    if boundary_tie:
+        assert int(g_L.sum()) == m
+    else:
+        np.testing.assert_array_equal(g_L, o_s.verify_len)
     prob.verify_len = o_s.verify_len.astype(np.int32)
-    orc = O.verify_problem(prob, all_rows=True)
-    rep = PU.compare("confidence -> schedule -> verify", res, orc, dtype=w.dtype)
+    same = np.nonzero(g_L == o_s.verify_len)[0]    # every sequence unless the stop is a near tie
+    orc = O.verify_problem(prob, seqs=same, all_rows=True)
+    rep = PU.compare("confidence -> schedule -> verify", res, orc, dtype=w.dtype, prob=prob)
     print(rep.line(), flush=True)
     assert not rep.mismatches, rep.mismatches[:5]
