@@ -18,7 +18,7 @@ SV_OK, SV_EINVAL, SV_ENOMEM, SV_EDEVICE, SV_EUNSUPPORTED = 0, -1, -2, -3, -4
 SV_F32, SV_BF16 = 0, 1
 SV_LEN_FIXED, SV_LEN_TAU = 0, 1
 SV_DRAFT_PROBS, SV_DRAFT_ONEHOT = 0, 1
-SV_STATUS_BAD_INPUT, SV_STATUS_TIMEOUT = 1, 2
+SV_STATUS_BAD_INPUT, SV_STATUS_INCOMPLETE = 1, 2
 
 EXPORTED = (
     "spec_verify_create", "spec_verify_check", "spec_verify_run", "spec_verify_destroy",
@@ -50,6 +50,7 @@ class Args(ctypes.Structure):
         ("residual_mass", ctypes.c_void_p), ("sampled_prob", ctypes.c_void_p), ("rows_read", ctypes.c_void_p),
         ("device_status", ctypes.c_void_p), ("draft_mode", ctypes.c_int32),
         ("target_row_offsets", ctypes.c_void_p), ("draft_row_offsets", ctypes.c_void_p),
+        ("bytes_read", ctypes.c_void_p),
     ]
 
 
@@ -141,7 +142,8 @@ def make_args(B: int, K: int, *, target, draft=None, tokens, uniforms=None, temp
               length_mode: int = SV_LEN_FIXED, verify_len=None, confidence=None, tau=None,
               accepted_len, out_tokens, verify_len_out, lse_target=None, lse_draft=None, survival=None,
               residual_mass=None, sampled_prob=None, rows_read=None, device_status=None,
-              draft_mode: int = SV_DRAFT_PROBS, target_row_offsets=None, draft_row_offsets=None) -> Args:
+              draft_mode: int = SV_DRAFT_PROBS, target_row_offsets=None, draft_row_offsets=None,
+              bytes_read=None) -> Args:
     """Fill an Args struct.  Strides are (batch, row) in elements."""
     return Args(
         B, K, _addr(target), int(target_strides[0]), int(target_strides[1]),
@@ -151,7 +153,7 @@ def make_args(B: int, K: int, *, target, draft=None, tokens, uniforms=None, temp
         _addr(accepted_len), _addr(out_tokens), _addr(verify_len_out),
         _addr(lse_target), _addr(lse_draft), _addr(survival), _addr(residual_mass), _addr(sampled_prob),
         _addr(rows_read), _addr(device_status), int(draft_mode), _addr(target_row_offsets),
-        _addr(draft_row_offsets))
+        _addr(draft_row_offsets), _addr(bytes_read))
 
 
 def check(cfg: Config, args: Args) -> int:

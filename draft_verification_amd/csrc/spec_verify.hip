@@ -10,51 +10,51 @@
 // built around 16-byte coalesced loads, wavefront shuffles and small LDS
 // reductions.
 //
-// Early exit.  The pages say generation restarts from the first error, so no
-// row after the first rejection can change the output.  Positions are walked
-// in groups (sizes 3, 3, 4, 8, 16, ... along the block); each group is two
-// plain launches:
-//   sv_rows    one workgroup per 16384-element split of every row the group
-//              needs (target and draft rows of sequences still open), reduced
-//              to (max, sum exp2) or (max, argmax) partials.  No atomics and no
-//              fences: the kernel boundary publishes the partials.  The last
-//              group from the fourth on, where few sequences are still open,
-//              runs as sv_rows_late (eight candidate rows per workgroup).
-//   sv_decide  one workgroup per open sequence: merges the partials of the
-//              group's positions in fp64 and walks them in order -- survival
-//              and verify length, the acceptance test u < p/q (or the greedy
-//              match) -- until the first rejection, the bonus row, or the end of
-//              the group.
-// Rows inside a group past a rejection are read speculatively (they lie within
-// the verify window).  Synchronising only at kernel boundaries keeps every
-// launch a pure stream: an agent-scope fence costs ~130 ns, serialised, on
-// this chip, so work is never handed between workgroups inside a launch.
-//
-// When the step samples with draft probabilities, the last group has no
-// sv_decide launch: sv_resid takes those decisions at its start.
-//
-// After the last group:
-//   sv_resid   per (sequence, split, half split): the last group's decisions
-//              (every workgroup of a sequence derives them; one writes them),
-//              then for a rejecting sequence the segment sums of
-//              max(0, p - q) over the rejected row pair.  (One-hot drafts have
-//              no residual pass: sv_draw forms p without x itself.)
+// Early exit inside one launch.  The pages say generation restarts from the
+// first error, so no row after the first rejection can change the output.
+// A step is four launches:
+//   sv_plan    per sequence: the verify length where it is known without
+//              logits, and the control words of the step.
+//   sv_stream  one workgroup per 16384-element split of every row the step may
+//              need, ordered position by position (all sequences' position 1,
+//              then position 2, ...).  A workgroup first reads its sequence's
+//              control word and exits if an earlier position has already been
+//              rejected (or the verify length excludes its row); otherwise it
+//              reduces its split to (max, sum exp2) or (max, argmax) partials.
+//              The last of a row's split workgroups to finish (an arrival
+//              counter) merges the row in fp64; the second of a position's two
+//              rows to finish takes the acceptance test u < p/q and, on a
+//              rejection, lowers the sequence's "first rejection" word, which
+//              later workgroups of the same launch read.  Rows of positions
+//              dispatched before the rejection was known are read anyway (they
+//              lie inside the verify window).  With a derived confidence and an
+//              open length walk, each merged draft row also advances the
+//              sequence's survival product S_j = S_{j-1} c_j as far as the
+//              merged rows allow, and closes the walk (fixes L) at the first
+//              S_j < tau.
+//   sv_resid   per (sequence, split, half split), for a sequence whose walk
+//              ended in a rejection: the segment sums of max(0, p - q) over the
+//              rejected row pair.  (One-hot drafts have no residual pass:
+//              sv_draw forms p without x itself.)
 //   sv_draw    per sequence: inverse-CDF draw (replacement or bonus) by split
-//              and segment prefix in fp64, then one segment's tokens scanned
-//              in token order; writes the outputs.
-// sv_plan (first) sets up per-sequence state and the verify length where it
-// is known without reading logits.
+//              and segment prefix in fp64, then one segment's tokens scanned in
+//              token order; writes the outputs.
+//
+// Workgroups of one launch exchange records only through agent-scope stores
+// and loads (coherent across the chip's eight L2 caches) and arrival counters:
+// a writer waits for its stores to complete before the atomic that hands them
+// over, so no L2 write-back fence is needed (that fence costs ~130 ns per
+// workgroup, serialised).  No workgroup ever waits for another: a workgroup
+// that is not last at a counter simply exits.
 //
 // Numerics.  bf16 and fp32 inputs are exact in fp32.  The row statistics take
 // one fma per element, l*c - round(m*c) with c = log2(e)/T in fp32, and keep
-// the exact rounding error of m*c beside the split sum for the fp64 merges;
-// the final draw forms a = (l - m) * log2(e)/T with the constant split in two
-// fp32 parts and scales by the rows' 1/S in two fp32 parts (no systematic scale
-// bias, which would not cancel in p - q).  v_exp_f32 measured on MI355X:
-// < 0.8 ulp for arguments >= -12.  Sums run in fp32 over 8 elements and in
-// fp64 beyond, so a row sum carries ~1e-8 relative error.
-// Decisions (acceptance ratio, survival product, CDF prefix) are taken in fp64.
-// The final draw evaluates large masses (> 2^-9) in fp64.
+// the exact rounding error of m*c beside the split sum for the fp64 merges.
+// v_exp_f32 measured on MI355X: < 0.8 ulp for arguments >= -12.  Sums run in
+// fp32 over 8 elements and in fp64 beyond.  Decisions (acceptance ratio,
+// survival product, CDF prefix) are taken in fp64.  The residual mass of a
+// token is p (1 - 2^-D) with D = log2(p/q) formed from the exact logit
+// difference, so it keeps its relative accuracy when p and q nearly agree.
 //
 // Determinism.  Split boundaries depend only on V, every reduction has a fixed
 // order and there are no floating-point atomics, so outputs are bitwise
@@ -69,6 +69,9 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
+#include <tuple>
+
 #include "spec_verify.h"
 
 namespace {
@@ -77,43 +80,50 @@ constexpr int kThreads = 256;                     // 4 wavefronts of 64
 constexpr int kWaves = kThreads / 64;
 constexpr int kSplit = 16384;                     // elements per split (fixed for batch invariance)
 constexpr int kPerLane = kSplit / kThreads;       // 64 elements per lane per split
-constexpr int kMaxGroup = 16;                     // positions per group
-constexpr int kMaxGroups = 64;                    // groups per step (K + 1 <= 2 + 2 + 4 + 8 + 16 * 59)
+constexpr int kChunkPos = 32;                     // positions per sv_stream launch
 
-enum { CTL_STATUS = 0, CTL_SCHED_STATUS = 1, CTL_CONF_STATUS = 2, CTL_WORDS = 64 };
-enum { FL_ACC = 1, FL_LEN = 2 };
+enum { CTL_STATUS = 0, CTL_DONE = 1, CTL_SCHED_STATUS = 2, CTL_CONF_STATUS = 3, CTL_WORDS = 64 };
+enum { SEQ_BAD = 1, SEQ_OPEN = 2 };               // plan-time flags of a sequence
+enum { DEC_REJECT = 2, DEC_BAD = 3 };             // decision of a position (written on rejection only)
 // Compile-time variants of the step kernels: MODE_ONEHOT (q is the point mass
 // at the drafted token; never with greedy verification) and MODE_PACKED (rows
 // addressed through per-sequence offsets).
 enum { MODE_ONEHOT = 1, MODE_PACKED = 2 };
-enum { KIND_NONE = -1, KIND_RESID = 0, KIND_BONUS = 1, KIND_GREEDY = 2, KIND_BAD = 3 };
-enum { K_PLAN = 0, K_ROWS = 1, K_DECIDE = 2, K_RESID = 3, K_DRAW = 4, K_COUNT = 5 };
+enum { KIND_RESID = 0, KIND_BONUS = 1, KIND_GREEDY = 2, KIND_BAD = 3 };
+enum { K_PLAN = 0, K_STREAM = 1, K_RESID = 2, K_DRAW = 3, K_COUNT = 4 };
+constexpr unsigned kUnread = 0x7fbadbadu;         // part_m bits of a split no workgroup streamed
 
-struct SeqState {
-    double S;      // survival product S_j of the positions evaluated so far
-    double St, Sd; // sums of exp2((l - M) c) of the rows of the final draw
-    float Mt, Md;  // maxima of those rows
-    int L;         // verify length, -1 while undetermined
-    int a;         // accepted positions so far
-    int flags;     // FL_ACC: acceptance walk open; FL_LEN: verify-length walk open
-    int kind;      // KIND_*
-    int js;        // 1-based row of the final draw
-    int y;         // token chosen by the walk (greedy)
-    int rows;      // logit rows streamed for this sequence
-    int pad;
+// Control word of a sequence.  dead: the first rejected (or bad) position
+// known so far, K + 2 while none (0 for a sequence marked bad at plan time);
+// lowered with atomic min.  lw: (L + 1) << 16 |
+// f, where L + 1 == 0 while the verify length is still open and f is the number
+// of survivals S_1..S_f the open walk has formed; moved with compare-and-swap.
+struct SeqCtl {
+    int dead;
+    int lw;
+    int flags;  // SEQ_*
+    int Lout;   // verify length as given (reported for a sequence marked bad)
 };
 
 struct Work {
     int* ctl;
+    SeqCtl* seq;      // [B]
+    int* rcnt;        // [B][2K+1] split arrivals per row (+1 once an open walk's draft row is stored)
+    int* pcnt;        // [B][K+2] arrivals per position (1 .. K+1): split workgroups of its rows (verify
+                      //   length known at plan time), or merged rows (open length walk)
+    int* dec;         // [B][K+1] DEC_* of a rejected or bad position
     float* part_m;    // [B][2K+1][nsplit] split maxima; row j-1 target, K+j draft (j 1-based)
     double* part_s;   // same layout, split sums of exp2((l - m) c + d)
     float* part_d;    // same layout, the d of that sum (the true split sum is part_s * 2^-d)
     int* part_i;      // same layout, split argmax (greedy)
-    SeqState* st;     // [max_batch]
-    SeqState* fin;    // [max_batch] state after the last group, stored by sv_resid (which takes its decisions)
-    int* live;        // [max_batch] (L + 1) << 2 | flags, the part of st that sv_rows reads
-    double* seg;      // [max_batch][nsplit][64] residual mass per segment of a split
-    float* xlog;      // [max_batch][2K+1] logit of the drafted token in each row
+    float* row_m;     // [B][2K+1] row maximum
+    double* row_s;    // [B][2K+1] row sum of exp2((l - row_m) c)
+    int* row_g;       // [B][2K+1] row argmax (greedy)
+    float* xlog;      // [B][2K+1] logit of the drafted token in each row
+    double* srec;     // [B][K] survivals S_j of an open length walk
+    double* seg;      // [B][nsplit][64] residual mass per segment of a split
+    double* segq;     // [B][nsplit][64] q on the residual's support per segment (nearly equal rows)
+    double* kp;       // [B][nsplit][2][4] renormalisation sums per half split (nearly equal rows)
 };
 
 // Workspace of the admission and confidence calls (kept out of Work so that the
@@ -130,9 +140,10 @@ struct AuxWork {
 };
 
 struct Params {
-    int B, K, V, nsplit, seg_w;   // seg_w: the power of two >= nsplit
+    int B, K, V, nsplit;
     int greedy, derived;       // derived: tau mode with c = max draft probability
     int onehot;                // q_j is the point mass at x_j; no draft row is streamed
+    int count;                 // mark streamed splits (rows_read / bytes_read asked for)
     const long long* toff;     // packed rows: target rows of sequence b start at row toff[b] (NULL: dense)
     const long long* doff;     // packed rows: draft rows of sequence b start at row doff[b]
     int len_mode;
@@ -157,14 +168,42 @@ struct Params {
     float* zmass;
     float* pys;
     int* rows_out;
+    long long* bytes_out;
     int* status_out;
 };
 
 __device__ __forceinline__ void or_status(int* p, int v) { __hip_atomic_fetch_or(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
 
+// Records handed between workgroups of one launch: agent-scope (coherent)
+// stores and loads, and the wait for a workgroup's own stores to complete
+// (s_waitcnt vmcnt(0)) before the atomic that publishes them.
+template <typename T>
+__device__ __forceinline__ T ld_ag(const T* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+template <typename T>
+__device__ __forceinline__ void st_ag(T* p, T v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+__device__ __forceinline__ void stores_done() { __builtin_amdgcn_s_waitcnt(0x0F70); } // vmcnt(0)
+__device__ __forceinline__ int add_ag(int* p, int v) { return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+__device__ __forceinline__ void min_ag(int* p, int v) { (void)__hip_atomic_fetch_min(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+__device__ __forceinline__ bool cas_ag(int* p, int expect, int desired)
+{
+    return __hip_atomic_compare_exchange_strong(p, &expect, desired, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __device__ __forceinline__ long long part_index(const Params& p, int b, int row)
 {
     return ((long long)b * (2 * p.K + 1) + row) * p.nsplit;
+}
+
+__device__ __forceinline__ long long row_index(const Params& p, int b, int row)
+{
+    return (long long)b * (2 * p.K + 1) + row;
+}
+
+// Arrival counter of position j (1 .. K + 1) of sequence b.
+__device__ __forceinline__ long long pos_index(const Params& p, int b, int j)
+{
+    return (long long)b * (p.K + 2) + j;
 }
 
 // ---------------------------------------------------------------- reductions
@@ -252,9 +291,8 @@ __device__ __forceinline__ void block_argmax(float& v, int& i, float* redf, int*
 
 // 16-byte load of streamed logits, marked non-temporal: the row statistics read
 // each row once per step and the residual pass reads the rejected row pairs
-// once, so their lines are not kept in the caches (measured: 23 us less per
-// verify step at B=256 K=16 V=129280 bf16, the row statistics at 5.5 TB/s
-// instead of 4.9).
+// once, so their lines are not kept in the caches (measured: the row
+// statistics at 5.5 TB/s instead of 4.9 at B=256 K=16 V=129280 bf16).
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ u32x4 load16_stream(const void* p) { return __builtin_nontemporal_load((const u32x4*)p); }
 
@@ -307,8 +345,8 @@ struct Chunk<SV_BF16> {
     }
     // Same data as load(), with every vector load issued unconditionally (the
     // address of a vector past V is clamped to the row's last vector) so that
-    // the number of loads in flight is fixed and a later chunk's loads need not
-    // be waited for; fix_tail() then sets the vectors past V to -inf.
+    // the number of loads in flight is fixed; fix_tail() then sets the vectors
+    // past V to -inf.
     template <bool VEC>
     __device__ __forceinline__ void issue(const void* row, int base, int V, int lane)
     {
@@ -498,21 +536,30 @@ __device__ __forceinline__ float scaled_exp2(float l, float m, float c_hi, float
 // 2^a in fp64: a = n + f with n = rint(a), |f| <= 1/2, and e^(f ln 2) from its
 // Taylor series to the x^11 term (|x| <= 0.347, truncation below 1e-14
 // relative), scaled by 2^n.  -inf and very negative a give 0; NaN passes.
+// An fp64 constant held in scalar registers (an fma takes one scalar operand):
+// inside loops the compiler would otherwise keep every coefficient below in a
+// pair of vector registers for the whole loop.
+__device__ __forceinline__ double sk(double c)
+{
+    asm("" : "+s"(c));
+    return c;
+}
+
 __device__ __forceinline__ double exp2_f64(double a)
 {
     if (!(a > -1100.0)) return a != a ? a : 0.0;
     if (a > 1100.0) return INFINITY;
     const double n = rint(a);
-    const double x = (a - n) * 0.69314718055994530942;
-    double r = 2.505210838544171877505e-08;    // 1/11!
-    r = fma(r, x, 2.755731922398589065256e-07); // 1/10!
-    r = fma(r, x, 2.755731922398589065256e-06); // 1/9!
-    r = fma(r, x, 2.480158730158730158730e-05); // 1/8!
-    r = fma(r, x, 1.984126984126984126984e-04); // 1/7!
-    r = fma(r, x, 1.388888888888888888889e-03); // 1/6!
-    r = fma(r, x, 8.333333333333333333333e-03); // 1/5!
-    r = fma(r, x, 4.166666666666666666667e-02); // 1/4!
-    r = fma(r, x, 1.666666666666666666667e-01); // 1/3!
+    const double x = (a - n) * sk(0.69314718055994530942);
+    double r = sk(2.505210838544171877505e-08);     // 1/11!
+    r = fma(r, x, sk(2.755731922398589065256e-07)); // 1/10!
+    r = fma(r, x, sk(2.755731922398589065256e-06)); // 1/9!
+    r = fma(r, x, sk(2.480158730158730158730e-05)); // 1/8!
+    r = fma(r, x, sk(1.984126984126984126984e-04)); // 1/7!
+    r = fma(r, x, sk(1.388888888888888888889e-03)); // 1/6!
+    r = fma(r, x, sk(8.333333333333333333333e-03)); // 1/5!
+    r = fma(r, x, sk(4.166666666666666666667e-02)); // 1/4!
+    r = fma(r, x, sk(1.666666666666666666667e-01)); // 1/3!
     r = fma(r, x, 0.5);
     r = fma(r, x, 1.0);
     r = fma(r, x, 1.0);
@@ -530,13 +577,15 @@ __device__ __forceinline__ double exp2_f64(double a)
 // bf16: the sum pass widens the packed words again with byte permutes rather
 // than reusing the max pass's shifts, so the 64 widened values are never live
 // at once (registers are what bound the loads in flight).
-__device__ __forceinline__ float bf16_lo_perm(uint32_t w) { return __uint_as_float(__builtin_amdgcn_perm(w, 0u, 0x05040c0cu)); }
-__device__ __forceinline__ float bf16_hi_perm(uint32_t w) { return __uint_as_float(__builtin_amdgcn_perm(w, 0u, 0x07060c0cu)); }
+__device__ __forceinline__ float bf16_perm(uint32_t w, uint32_t sel) { return __uint_as_float(__builtin_amdgcn_perm(w, 0u, sel)); }
 
+// Element e of a loaded split for the sum pass; sel_lo and sel_hi are the byte
+// selectors of the low and high bf16 half, passed in opaquely per run so that
+// no widening is moved out of its run.
 template <int DT>
-__device__ __forceinline__ float chunk_elem_sum(const Chunk<DT>& c, int e)
+__device__ __forceinline__ float chunk_elem_sum(const Chunk<DT>& c, int e, uint32_t sel_lo, uint32_t sel_hi)
 {
-    if (DT == SV_BF16) return (e & 1) ? bf16_hi_perm(((const uint32_t*)&c)[e >> 1]) : bf16_lo_perm(((const uint32_t*)&c)[e >> 1]);
+    if (DT == SV_BF16) return bf16_perm(((const uint32_t*)&c)[e >> 1], (e & 1) ? sel_hi : sel_lo);
     return c.get(e);
 }
 
@@ -556,18 +605,22 @@ __device__ __forceinline__ void chunk_stats(const Chunk<DT>& c, float c32, float
             d = fmaf(m, c32, -mc);
 #pragma unroll
             for (int r = 0; r < kPerLane / 8; ++r) {
+                uint32_t lo = 0x05040c0cu, hi = 0x07060c0cu;
+                asm volatile("" : "+s"(lo), "+s"(hi)); // widen one run at a time
                 float run = 0.0f;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) run += __builtin_amdgcn_exp2f(fmaf(chunk_elem_sum<DT>(c, 8 * r + i), c32, -mc));
+                for (int i = 0; i < 8; ++i) run += __builtin_amdgcn_exp2f(fmaf(chunk_elem_sum<DT>(c, 8 * r + i, lo, hi), c32, -mc));
                 acc += (double)run;
-                __builtin_amdgcn_sched_barrier(0); // widen one run at a time
+                __builtin_amdgcn_sched_barrier(0);
             }
         } else {
 #pragma unroll
             for (int r = 0; r < kPerLane / 8; ++r) {
+                uint32_t lo = 0x05040c0cu, hi = 0x07060c0cu;
+                asm volatile("" : "+s"(lo), "+s"(hi));
                 float run = 0.0f;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) run += scaled_exp2(chunk_elem_sum<DT>(c, 8 * r + i), m, c_hi, c_lo);
+                for (int i = 0; i < 8; ++i) run += scaled_exp2(chunk_elem_sum<DT>(c, 8 * r + i, lo, hi), m, c_hi, c_lo);
                 acc += (double)run;
             }
         }
@@ -596,23 +649,27 @@ __device__ __forceinline__ void chunk_argmax(const Chunk<DT>& c, int V, int spli
 }
 
 // ---------------------------------------------------------------- sv_plan
+//
+// One thread per (sequence, row): clears the row's arrival counter (and the
+// position's), marks the row's splits unread when the caller counts streamed
+// bytes; the thread of row 0 sets the sequence's control word.
 
 __global__ __launch_bounds__(kThreads) void sv_plan_kernel(Params p, Work w)
 {
+    const long long R = 2LL * p.K + 1;
     const long long i = (long long)blockIdx.x * kThreads + threadIdx.x;
-    if (i >= p.B) return;
-    const int b = (int)i, K = p.K;
-    SeqState st;
-    st.S = 1.0;
-    st.St = st.Sd = 0.0;
-    st.Mt = st.Md = 0.0f;
-    st.a = 0;
-    st.kind = KIND_NONE;
-    st.js = 0;
-    st.y = -1;
-    st.rows = 0;
-    st.pad = 0;
-    bool bad = false, len_open = false;
+    if (i >= (long long)p.B * R) return;
+    const int b = (int)(i / R), r = (int)(i % R), K = p.K;
+    w.rcnt[i] = 0;
+    if (r <= K + 1) w.pcnt[pos_index(p, b, r)] = 0; // positions 1 .. K + 1 (R = 2K + 1 >= K + 2)
+    if (p.count)
+        for (int k = 0; k < p.nsplit; ++k) w.part_m[i * p.nsplit + k] = __uint_as_float(kUnread);
+    if (i == 0) {
+        w.ctl[CTL_STATUS] = 0; // every status bit of this call is raised by sv_draw
+        w.ctl[CTL_DONE] = 0;
+    }
+    if (r != 0) return;
+    bool bad = false, open = false;
     int L;
     if (p.toff) {
         // packed rows: the sequence brings L + 1 target rows (and L draft rows)
@@ -639,462 +696,396 @@ __global__ __launch_bounds__(kThreads) void sv_plan_kernel(Params p, Work w)
         const float tau = p.tau[b];
         if (!(tau <= 1.0f)) L = 0;
         else if (tau <= 0.0f || p.onehot) L = K; // one-hot drafts: c_j = 1
-        else { L = -1; len_open = true; }
+        else { L = -1; open = true; }
         if (p.onehot && p.surv)
             for (int j = 0; j < K; ++j) p.surv[(long long)b * K + j] = 1.0f;
     }
-    st.L = L;
-    if (bad) {
-        st.kind = KIND_BAD;
-        st.flags = 0;
-        or_status(&w.ctl[CTL_STATUS], SV_STATUS_BAD_INPUT);
-    } else {
-        st.flags = FL_ACC | (len_open ? FL_LEN : 0);
-    }
-    w.st[b] = st;
-    w.live[b] = st.flags ? (((st.L + 1) << 2) | st.flags) : 0;
+    SeqCtl c;
+    c.dead = bad ? 0 : K + 2; // a bad sequence needs no row
+    c.lw = (bad || open) ? 0 : ((L + 1) << 16);
+    c.flags = (bad ? SEQ_BAD : 0) | (open ? SEQ_OPEN : 0);
+    c.Lout = L;
+    w.seq[b] = c;
 }
 
-// ---------------------------------------------------------------- sv_rows
+// ---------------------------------------------------------------- sv_stream
 //
-// Which rows of a group are streamed, from the state at the start of the group:
-//   target row j  iff the acceptance walk is open and (L unknown or j <= L+1)
-//   draft row j   iff j <= K and (the length walk is open, or the acceptance
-//                 walk is open and j <= L)
-// sv_decide uses the same state, so every row its walk touches was streamed.
+// Which rows a workgroup streams, from its sequence's control word when it
+// starts (dead = first known rejection, L = verify length or unknown):
+//   target row j  iff j <= dead and (L unknown or j <= L + 1)
+//   draft row j   iff j <= K and (L unknown, or j <= min(dead, L))
+// With L unknown (an open length walk) every draft row feeds the survival
+// product; once the walk closes, only the tested positions' draft rows are read.
 
-__device__ __forceinline__ bool target_row_needed(int flags, int L, int j, int K)
+// Survival walk of an open verify length (derived confidence c_j = 1/Sd_j):
+// advances S_f -> S_{f+1} = S_f c_{f+1} while the next draft row's statistics
+// are stored, and closes the walk at the first S_j < tau (L = j - 1) or at K.
+// Any thread that finds the next row ready may take the step (compare-and-swap
+// on the control word; a racing thread computes the same value); a thread that
+// finds it not ready leaves, and the thread that stores that row continues.
+// Bounded: every failed swap means another thread advanced the walk.
+__device__ void advance_survival(const Params& p, const Work& w, int b)
 {
-    return (flags & FL_ACC) && j <= K + 1 && (L < 0 || j <= L + 1);
-}
-
-__device__ __forceinline__ bool draft_row_needed(int flags, int L, int j, int K)
-{
-    return j <= K && ((flags & FL_LEN) || ((flags & FL_ACC) && j <= L));
-}
-
-// One split of one needed row: (max, sum exp2) or (max, argmax) partials, and
-// the drafted token's logit when the split holds it.
-struct RowRef {
-    const void* row;
-    int b, j, prow, split;
-};
-
-template <int DT, bool PK>
-__device__ __forceinline__ RowRef row_ref(const Params& p, int b, int j, bool draft, int split)
-{
-    RowRef r;
-    r.row = draft ? seq_row<DT, PK>(p.d, p.doff, p.dbs, p.drs, b, j - 1)
-                  : seq_row<DT, PK>(p.t, p.toff, p.tbs, p.trs, b, j - 1);
-    r.b = b;
-    r.j = j;
-    r.prow = draft ? p.K + j : j - 1;
-    r.split = split;
-    return r;
-}
-
-// t: thread index inside the workgroup.
-template <int DT, bool GREEDY>
-__device__ __forceinline__ void rows_finish(const Params& p, const Work& w, const Chunk<DT>& c, const RowRef& r,
-                                            float* redf, double* redd, int* redi, int t)
-{
-    const long long pi = part_index(p, r.b, r.prow) + r.split;
-    if (GREEDY) {
-        float M;
-        int I;
-        chunk_argmax<DT>(c, p.V, r.split, M, I, redf, redi, t);
-        if (t == 0) {
-            w.part_m[pi] = M;
-            w.part_i[pi] = I;
-        }
-    } else {
-        // the drafted token of this position and its logit in this row, when
-        // the split holds it: r.b, r.j and x are uniform, so both come through
-        // scalar loads (the token ids and logits are never written here)
-        if (r.j <= p.K) {
-            typedef const __attribute__((address_space(4))) uint32_t* cptr;
-            const int x = (int)((cptr)p.tok)[(long long)r.b * p.K + (r.j - 1)];
-            const int off = x - r.split * kSplit;
-            if (x >= 0 && x < p.V && off >= 0 && off < kSplit) {
-                float xl;
-                if (DT == SV_BF16) {
-                    // the aligned word holding element x lies in the same page
-                    const uintptr_t a = (uintptr_t)r.row + 2 * (uintptr_t)x;
-                    const uint32_t word = *(cptr)(a & ~(uintptr_t)3);
-                    xl = (a & 2) ? bf16_hi(word) : bf16_lo(word);
-                } else {
-                    xl = __uint_as_float(((cptr)r.row)[x]);
-                }
-                if (t == 0) w.xlog[(long long)r.b * (2 * p.K + 1) + r.prow] = xl;
-            }
-        }
-        float M, D;
-        double S;
-        chunk_stats<DT>(c, p.c32, p.c_hi, p.c_lo, M, S, D, redf, redd, t);
-        if (t == 0) {
-            w.part_m[pi] = M;
-            w.part_s[pi] = S;
-            w.part_d[pi] = D;
-        }
+    const double tau = (double)p.tau[b];
+    const int K = p.K, ns = p.nsplit;
+    int* lwp = &w.seq[b].lw;
+    for (int it = 0; it <= 2 * K + 2; ++it) {
+        const int lw = ld_ag(lwp);
+        if (lw >> 16) return;          // closed
+        const int f = lw & 0xffff;     // S_1 .. S_f formed
+        if (f >= K) return;
+        if (ld_ag(&w.rcnt[row_index(p, b, K + f + 1)]) != ns + 1) return; // c_{f+1} not stored yet
+        const double Sd = ld_ag(&w.row_s[row_index(p, b, K + f + 1)]);
+        const double Sp = f ? ld_ag(&w.srec[(long long)b * K + f - 1]) : 1.0;
+        const double S = Sp / Sd;      // c = max_v q(v) = 1 / Sd
+        st_ag(&w.srec[(long long)b * K + f], S);
+        stores_done();
+        int nw;
+        if (S < tau) nw = ((f + 1) << 16) | (f + 1);   // L = f
+        else if (f + 1 == K) nw = ((K + 1) << 16) | K; // L = K
+        else nw = f + 1;
+        (void)cas_ag(lwp, lw, nw);
     }
 }
 
-// One workgroup per (sequence, row slot, split), split fastest, so that
-// consecutive workgroups stream consecutive 32 KB pieces of a row (HBM keeps
-// its rate on long contiguous runs).  A workgroup of a row the walk does not
-// need exits after one scalar load.
+// Merge of one row's split partials in fp64, fixed order (wave 0; lane k
+// holds split k's partials, other lanes hold (-inf, 0)).
+__device__ __forceinline__ void merge_stats(const Params& p, float pm, double ps, float pd, int lane, float& M, double& S)
+{
+    M = wave_max(pm);
+    const double v = (lane < p.nsplit && pm != -INFINITY) ? ps * exp2_f64(((double)pm - (double)M) * p.c64 - (double)pd) : 0.0;
+    S = wave_sum(v);
+}
+
+// Acceptance test of position j: accept the drafted token iff u_j <
+// p_j(x_j) / q_j(x_j), the ratio from exact logit differences and the fp64 row
+// sums (q(x) = 0 accepts).  Returns 0 (accept) or DEC_REJECT.
+__device__ __forceinline__ int accept_test(const Params& p, float u, float xt, float Mt, double St, float xd, float Md,
+                                           double Sd)
+{
+    double ratio = INFINITY;
+    if (xd != -INFINITY) ratio = exp2_f64((((double)xt - (double)Mt) - ((double)xd - (double)Md)) * p.c64) * (Sd / St);
+    return ((double)u < ratio) ? 0 : DEC_REJECT;
+}
+
+__device__ __forceinline__ void record_rejection(const Work& w, const Params& p, int b, int j, int dec)
+{
+    st_ag(&w.dec[(long long)b * (p.K + 1) + j], dec);
+    min_ag(&w.seq[b].dead, j);
+}
+
+// Verify length known at plan time: the last split workgroup of position j
+// (wave 0 only) merges the position's rows -- the target row, and the draft
+// row when j <= L -- stores their records and takes the decision of a tested
+// position (j <= L): the greedy match, or u < p(x)/q(x) (q(x) = 1 for a
+// one-hot draft).  x and u are the drafted token and its uniform.
+template <bool GREEDY, int MODE>
+__device__ void position_complete(const Params& p, const Work& w, int b, int j, int L, int lane, int x, float u)
+{
+    constexpr bool OH = (MODE & MODE_ONEHOT) != 0;
+    const int K = p.K, ns = p.nsplit;
+    const bool two = !GREEDY && !OH && j <= L;
+    const long long pt = part_index(p, b, j - 1), pd_ = part_index(p, b, K + j);
+    // every partial of the position in one round trip
+    float mt = -INFINITY, md = -INFINITY, dt = 0.0f, dd = 0.0f, xt = 0.0f, xd = 0.0f;
+    double st = 0.0, sd = 0.0;
+    int it = 0x7fffffff;
+    if (lane < ns) {
+        mt = ld_ag(&w.part_m[pt + lane]);
+        if (GREEDY) {
+            it = ld_ag(&w.part_i[pt + lane]);
+        } else {
+            st = ld_ag(&w.part_s[pt + lane]);
+            dt = ld_ag(&w.part_d[pt + lane]);
+        }
+        if (two) {
+            md = ld_ag(&w.part_m[pd_ + lane]);
+            sd = ld_ag(&w.part_s[pd_ + lane]);
+            dd = ld_ag(&w.part_d[pd_ + lane]);
+        }
+    }
+    const bool tested = j <= K && j <= L && x >= 0 && x < p.V;
+    if (!GREEDY && tested && lane == 0) {
+        xt = ld_ag(&w.xlog[row_index(p, b, j - 1)]);
+        if (two) xd = ld_ag(&w.xlog[row_index(p, b, K + j)]);
+    }
+    float Mt, Md = 0.0f;
+    double St = 0.0, Sd = 1.0;
+    int G = 0;
+    if (GREEDY) {
+        float v = mt;
+        int ix = it;
+        wave_argmax(v, ix);
+        Mt = v;
+        G = ix;
+    } else {
+        merge_stats(p, mt, st, dt, lane, Mt, St);
+        if (two) merge_stats(p, md, sd, dd, lane, Md, Sd);
+    }
+    if (lane != 0) return;
+    const long long rt = row_index(p, b, j - 1);
+    w.row_m[rt] = Mt;
+    if (GREEDY) w.row_g[rt] = G;
+    else w.row_s[rt] = St;
+    if (two) {
+        w.row_m[row_index(p, b, K + j)] = Md;
+        w.row_s[row_index(p, b, K + j)] = Sd;
+    }
+    if (j > K || j > L) return; // the bonus row: no test
+    int dec;
+    if (x < 0 || x >= p.V) dec = DEC_BAD;
+    else if (GREEDY) dec = x == G ? 0 : DEC_REJECT;
+    else if (OH) dec = accept_test(p, u, xt, Mt, St, 0.0f, 0.0f, 1.0); // one-hot draft row: max 0, sum 1
+    else dec = accept_test(p, u, xt, Mt, St, xd, Md, Sd);
+    if (dec) record_rejection(w, p, b, j, dec);
+}
+
+// Open length walk (derived confidence, 0 < tau <= 1): the last split
+// workgroup of a row (wave 0 only) merges that row and publishes its record.
+// A draft row then advances the survival walk; the second of a position's two
+// rows takes the acceptance test (a test past the L the walk settles on is
+// ignored by the final state).
+__device__ void row_complete_open(const Params& p, const Work& w, int b, int j, bool draft, int prow, int lane, int x,
+                                  float u)
+{
+    const int K = p.K, ns = p.nsplit;
+    const long long pb = part_index(p, b, prow), ri = row_index(p, b, prow);
+    float pm = -INFINITY, pd = 0.0f;
+    double ps = 0.0;
+    if (lane < ns) {
+        pm = ld_ag(&w.part_m[pb + lane]);
+        ps = ld_ag(&w.part_s[pb + lane]);
+        pd = ld_ag(&w.part_d[pb + lane]);
+    }
+    float M;
+    double S;
+    merge_stats(p, pm, ps, pd, lane, M, S);
+    if (lane != 0) return;
+    st_ag(&w.row_m[ri], M);
+    st_ag(&w.row_s[ri], S);
+    stores_done();
+    if (draft) {
+        (void)add_ag(&w.rcnt[ri], 1); // the row's statistics are stored: ns + 1
+        advance_survival(p, w, b);
+    }
+    if (j > K || add_ag(&w.pcnt[pos_index(p, b, j)], 1) != 1) return;
+    int dec;
+    if (x < 0 || x >= p.V) {
+        dec = DEC_BAD;
+    } else {
+        const long long rt = row_index(p, b, j - 1), rd = row_index(p, b, K + j);
+        const float Mt = ld_ag(&w.row_m[rt]), Md = ld_ag(&w.row_m[rd]);
+        const double St = ld_ag(&w.row_s[rt]), Sd = ld_ag(&w.row_s[rd]);
+        dec = accept_test(p, u, ld_ag(&w.xlog[rt]), Mt, St, ld_ag(&w.xlog[rd]), Md, Sd);
+    }
+    if (dec) record_rejection(w, p, b, j, dec);
+}
+
+// Streams split `split` of row (b, j, draft), which the sequence needs, and
+// hands its partials over.  Returns true in wave 0 when this was the last
+// arrival at the position's (or, in an open length walk, the row's) counter:
+// then the caller completes it (complete_row) with the drafted token x and its
+// uniform u returned here.  flags and L1 = L + 1 (0 while unknown) come from
+// the sequence's control word.  t: the thread index (re-derived by each caller
+// copy).
 template <int DT, bool VEC, bool GREEDY, int MODE>
-__global__ __launch_bounds__(kThreads, (DT == SV_BF16 && VEC) ? 8 : 1) void sv_rows_kernel(Params p, Work w, int j0,
-                                                                                           int G)
+__device__ __forceinline__ bool stream_row(const Params& p, const Work& w, int b, int j, bool draft, int split,
+                                           int flags, int L1, float* redf, double* redd, int* redi, int t, int& x_out,
+                                           float& u_out)
 {
     constexpr bool OH = (MODE & MODE_ONEHOT) != 0, PK = (MODE & MODE_PACKED) != 0;
+    constexpr int SLOTS = (GREEDY || OH) ? 1 : 2;
+    const int K = p.K;
+    const int prow = draft ? K + j : j - 1;
+    const void* row = draft ? seq_row<DT, PK>(p.d, p.doff, p.dbs, p.drs, b, j - 1)
+                            : seq_row<DT, PK>(p.t, p.toff, p.tbs, p.trs, b, j - 1);
+    Chunk<DT> c;
+    c.template issue<VEC>(row, split * kSplit, p.V, t);
+    c.template fix_tail<VEC>(split * kSplit, p.V, t);
+    // the drafted token of this position, its uniform, and its logit in this
+    // row when the split holds it: b, j and x are uniform, so all come through
+    // scalar loads (the token ids, uniforms and logits are never written here)
+    typedef const __attribute__((address_space(4))) uint32_t* cptr;
+    int x = -1;
+    float u = 0.0f, xl = 0.0f;
+    bool hasx = false;
+    if (j <= K) {
+        x = (int)((cptr)p.tok)[(long long)b * K + (j - 1)];
+        if (!GREEDY) u = __uint_as_float(((cptr)p.u)[(long long)b * (K + 1) + (j - 1)]);
+        const int off = x - split * kSplit;
+        if (!GREEDY && x >= 0 && x < p.V && off >= 0 && off < kSplit) {
+            if (DT == SV_BF16) {
+                // the aligned word holding element x lies in the same page
+                const uintptr_t a = (uintptr_t)row + 2 * (uintptr_t)x;
+                const uint32_t word = *(cptr)(a & ~(uintptr_t)3);
+                xl = (a & 2) ? bf16_hi(word) : bf16_lo(word);
+            } else {
+                xl = __uint_as_float(((cptr)row)[x]);
+            }
+            hasx = true;
+        }
+    }
+    const long long pi = part_index(p, b, prow) + split;
+    float M, D = 0.0f;
+    double S = 0.0;
+    int I = 0;
+    if (GREEDY) chunk_argmax<DT>(c, p.V, split, M, I, redf, redi, t);
+    else chunk_stats<DT>(c, p.c32, p.c_hi, p.c_lo, M, S, D, redf, redd, t);
+    x_out = x;
+    u_out = u;
+    if (t >= 64) return false; // wave 0 hands the partials over
+    const bool open = (flags & SEQ_OPEN) != 0;
+    int* ctr = open ? &w.rcnt[row_index(p, b, prow)] : &w.pcnt[pos_index(p, b, j)];
+    const int expect = p.nsplit * ((!open && SLOTS == 2 && j <= L1 - 1) ? 2 : 1);
+    int old = 0;
+    if (t == 0) {
+        st_ag(&w.part_m[pi], M);
+        if (GREEDY) {
+            st_ag(&w.part_i[pi], I);
+        } else {
+            st_ag(&w.part_s[pi], S);
+            st_ag(&w.part_d[pi], D);
+        }
+        if (hasx) st_ag(&w.xlog[row_index(p, b, prow)], xl);
+        stores_done();
+        old = add_ag(ctr, 1);
+    }
+    old = __builtin_amdgcn_readfirstlane(old);
+    return old == expect - 1;
+}
+
+// Completion of the last arrival (wave 0; lane = thread index).
+template <bool GREEDY, int MODE>
+__device__ __forceinline__ void complete_row(const Params& p, const Work& w, int b, int j, bool draft, int flags, int L1,
+                                             int lane, int x, float u)
+{
+    constexpr bool OH = (MODE & MODE_ONEHOT) != 0;
+    if constexpr (!GREEDY && !OH) {
+        if (flags & SEQ_OPEN) {
+            row_complete_open(p, w, b, j, draft, draft ? p.K + j : j - 1, lane, x, u);
+            return;
+        }
+    }
+    position_complete<GREEDY, MODE>(p, w, b, j, L1 - 1, lane, x, u);
+}
+
+
+// A sequence's control word (dead, lw) as read now, one agent-scope load
+// shared through LDS so that all waves of the workgroup see the same value.
+__device__ __forceinline__ unsigned long long control_word(const Work& w, int b, int t)
+{
+    __shared__ unsigned long long s_cw;
+    if (t == 0) s_cw = ld_ag((const unsigned long long*)&w.seq[b]);
+    __syncthreads();
+    const unsigned long long cw = s_cw;
+    __syncthreads(); // (the next read may overwrite it)
+    return cw;
+}
+
+// Whether a sequence needs row (j, draft) given its control word as read now
+// (dead = first known rejection, L1 = L + 1 or 0 while unknown):
+//   target row j  iff j <= dead and (L unknown or j <= L + 1)
+//   draft row j   iff j <= K and (L unknown, or j <= min(dead, L))
+// With L unknown (an open length walk) every draft row feeds the survival
+// product; once the walk closes, only the tested positions' draft rows are read.
+__device__ __forceinline__ bool row_needed(int K, int j, bool draft, int dead, int L1)
+{
+    return draft ? (j <= K && (L1 == 0 || j <= min(dead, L1 - 1))) : (j <= dead && (L1 == 0 || j <= L1));
+}
+
+// The row statistics with in-launch decisions, over positions j0 .. j0 +
+// gridDim.x / (B rows ns) - 1: one workgroup per (position, sequence, row,
+// split), split fastest, then the sequence's rows, then sequences, then
+// positions.  Consecutive workgroups stream consecutive 32 KB pieces of a row,
+// and a sequence's next position is a whole position block later, by when its
+// previous position is usually decided.  A workgroup whose row is no longer
+// needed exits after reading its sequence's control word.  Measured
+// alternatives, all slower at B=256 K=16 V=129280: dealing several rows to one
+// workgroup (one control-word load for several rows, but their decisions come
+// later, so more rows are read past a rejection: +40 us); a resident grid that
+// strides through the same task order and skips stopped sequences without a
+// dispatch each (it runs ahead of the decisions: 1.05 GB read instead of
+// 0.75, +100 us); walkers that stream one (sequence, row, split) from
+// position to position (each sequence's work serialised: +50 us).
+template <int DT, bool VEC, bool GREEDY, int MODE>
+__global__ __launch_bounds__(kThreads, (DT == SV_BF16 && VEC) ? 8 : 1) void sv_stream_kernel(Params p, Work w, int j0)
+{
+    constexpr bool OH = (MODE & MODE_ONEHOT) != 0;
+    constexpr int SLOTS = (GREEDY || OH) ? 1 : 2; // one-hot drafts: target rows only
     __shared__ float redf[kWaves];
     __shared__ double redd[kWaves];
     __shared__ int redi[kWaves];
     const int t = (int)threadIdx.x;
-    const int split = (int)(blockIdx.x % (unsigned)p.nsplit);
-    const int rest = (int)(blockIdx.x / (unsigned)p.nsplit);
-    const int slots = (GREEDY || OH) ? G : 2 * G; // one-hot drafts: target rows only
-    const int slot = rest % slots;
-    const int b = rest / slots;
-    const bool draft = !GREEDY && slot >= G;
-    const int j = j0 + (draft ? slot - G : slot);
-    typedef const __attribute__((address_space(4))) int* cptr;
-    const int lv = ((cptr)w.live)[b];
-    const int flags = lv & 3, L = (lv >> 2) - 1;
-    const bool need = draft ? draft_row_needed(flags, L, j, p.K) : target_row_needed(flags, L, j, p.K);
-    if (!need) return;
-    const RowRef r = row_ref<DT, PK>(p, b, j, draft, split);
-    Chunk<DT> c;
-    c.template issue<VEC>(r.row, split * kSplit, p.V, t);
-    c.template fix_tail<VEC>(split * kSplit, p.V, t);
-    rows_finish<DT, GREEDY>(p, w, c, r, redf, redd, redi, t);
+    const unsigned ns = (unsigned)p.nsplit;
+    const int split = (int)(blockIdx.x % ns);
+    unsigned rest = blockIdx.x / ns;
+    const bool draft = SLOTS == 2 && (rest & 1);
+    rest /= SLOTS;
+    const int b = (int)(rest % (unsigned)p.B);
+    const int j = j0 + (int)(rest / (unsigned)p.B);
+    // the sequence's control word as this workgroup starts: dead and lw in one
+    // load (a sequence marked bad at plan time has dead = 0), read once and
+    // shared so that every wave takes the same decision
+    const unsigned long long cw = control_word(w, b, t);
+    const int dead = (int)(unsigned)cw, L1 = (int)(cw >> 48);
+    if (!row_needed(p.K, j, draft, dead, L1)) return;
+    const int flags = w.seq[b].flags; // set by sv_plan
+    int x;
+    float u;
+    if (stream_row<DT, VEC, GREEDY, MODE>(p, w, b, j, draft, split, flags, L1, redf, redd, redi, t, x, u))
+        complete_row<GREEDY, MODE>(p, w, b, j, draft, flags, L1, t, x, u);
 }
 
-// The same statistics for the last position group from the fourth group on,
-// where the walks of most sequences have ended (typically a few in a hundred
-// are still open) and one workgroup per row would mostly start only to find
-// its row unneeded.  The group's rows (sequence, row slot) are dealt to nw =
-// gridDim.x / nsplit workgroup columns: column c takes rows c, c + nw, ...,
-// kRowsLate of them.  Lanes 0 .. kRowsLate-1 read those sequences' states at
-// once, and the workgroup streams the needed ones in turn.  Each turn is a
-// separate straight-line copy of the row code (a schedule barrier between
-// copies, the thread index re-derived in each) so that the copies neither
-// share registers nor overlap: registers bound the loads in flight.
-// (8 measured best for the last group at 4% of sequences open; 2 or 4 rows per
-// workgroup lost on a group with a quarter of them open, as one row per
-// workgroup then keeps more rows in flight.)
-constexpr int kRowsLate = 8;
-
-template <int DT, bool VEC, bool GREEDY, int MODE>
-__global__ __launch_bounds__(kThreads, (DT == SV_BF16 && VEC) ? 8 : 1) void sv_rows_late_kernel(Params p, Work w,
-                                                                                                int j0, int G)
-{
-    constexpr bool OH = (MODE & MODE_ONEHOT) != 0, PK = (MODE & MODE_PACKED) != 0;
-    __shared__ float redf[kWaves];
-    __shared__ double redd[kWaves];
-    __shared__ int redi[kWaves];
-    const int t = (int)threadIdx.x, lane = t & 63;
-    const int split = (int)(blockIdx.x % (unsigned)p.nsplit);
-    const int col = (int)(blockIdx.x / (unsigned)p.nsplit);
-    const int nw = (int)(gridDim.x / (unsigned)p.nsplit);
-    const int slots = (GREEDY || OH) ? G : 2 * G;
-    const int nrow = p.B * slots;
-    bool need = false;
-    if (lane < kRowsLate) {
-        const int i = col + lane * nw;
-        if (i < nrow) {
-            const int b = i / slots, slot = i % slots;
-            const int lv = w.live[b];
-            const int flags = lv & 3, L = (lv >> 2) - 1;
-            const bool draft = !GREEDY && slot >= G;
-            const int j = j0 + (draft ? slot - G : slot);
-            need = draft ? draft_row_needed(flags, L, j, p.K) : target_row_needed(flags, L, j, p.K);
-        }
-    }
-    const unsigned long long mask = __ballot(need); // the same in every wavefront
-    const int wv = __builtin_amdgcn_readfirstlane(t >> 6);
-#pragma unroll
-    for (int k = 0; k < kRowsLate; ++k) {
-        __builtin_amdgcn_sched_barrier(0);
-        if ((mask >> k) & 1) {
-            const int i = col + k * nw;
-            const int b = i / slots, slot = i % slots;
-            const bool draft = !GREEDY && slot >= G;
-            const int j = j0 + (draft ? slot - G : slot);
-            int z = 0;
-            asm volatile("" : "+v"(z)); // opaque: the index below is computed afresh in this copy
-            const int tl = (wv << 6) | (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, (unsigned)z));
-            const RowRef r = row_ref<DT, PK>(p, b, j, draft, split);
-            Chunk<DT> c;
-            c.template issue<VEC>(r.row, split * kSplit, p.V, tl);
-            c.template fix_tail<VEC>(split * kSplit, p.V, tl);
-            rows_finish<DT, GREEDY>(p, w, c, r, redf, redd, redi, tl);
-        }
-    }
-}
-
-// ---------------------------------------------------------------- sv_decide
+// ---------------------------------------------------------------- final state
 //
-// One workgroup per sequence.  Threads take (position, row, split) triples and
-// merge the split partials with fixed-order shuffles inside groups of sw lanes
-// (sw = the power of two >= nsplit), so every partial of the group is loaded in
-// one round trip; other threads gather the drafted tokens' logits.  Thread 0
-// then walks the positions in order.
+// The outcome of a sequence's walk, from its control word after the stream:
+// the first rejection r (if r <= L) ends the walk with a replacement draw from
+// row pair r (greedy: the target's token of row r), otherwise every verified
+// position was accepted and the bonus token comes from target row L + 1.
 
-__device__ __forceinline__ float seg_max(float v, int sw)
-{
-    for (int o = sw >> 1; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-    return v;
-}
-
-__device__ __forceinline__ double seg_sum(double v, int sw)
-{
-    for (int o = sw >> 1; o > 0; o >>= 1) v += __shfl_xor(v, o);
-    return v;
-}
-
-__device__ __forceinline__ void seg_argmax(float& v, int& i, int sw)
-{
-    for (int o = sw >> 1; o > 0; o >>= 1) {
-        const float ov = __shfl_xor(v, o);
-        const int oi = __shfl_xor(i, o);
-        if (ov > v || (ov == v && oi < i)) { v = ov; i = oi; }
-    }
-}
-
-struct DecideSmem {
-    float sMt[kMaxGroup], sMd[kMaxGroup], sLt[kMaxGroup], sLd[kMaxGroup];
-    double sSt[kMaxGroup], sSd[kMaxGroup];
-    int sG[kMaxGroup];
-    double sRatio[kMaxGroup];
-    float sLseT[kMaxGroup], sLseD[kMaxGroup];
-    int sTok[kMaxGroup];
-    float sU[kMaxGroup];
-    SeqState st;
+struct Final {
+    int kind, a, L, js, y;
+    bool bad_dec;  // marked bad by a drafted id outside [0, V) at a tested position
 };
 
-// The decisions of sequence b over positions j0 .. j0+G-1, from the state
-// before the group (w.st); every thread of the workgroup calls it and gets the
-// state after the group, which the caller stores.  writer: this workgroup
-// writes the decisions' outputs (lse and survival rows, status bits); other
-// callers only learn the result.
-template <int DT, bool GREEDY, int MODE>
-__device__ SeqState decide_group(const Params& p, const Work& w, int b, int j0, int G, bool writer, DecideSmem& sm)
+__device__ __forceinline__ Final final_state(const Params& p, const Work& w, int b, bool greedy)
 {
-    constexpr bool OH = (MODE & MODE_ONEHOT) != 0;
-    float* const sMt = sm.sMt;
-    float* const sMd = sm.sMd;
-    float* const sLt = sm.sLt;
-    float* const sLd = sm.sLd;
-    double* const sSt = sm.sSt;
-    double* const sSd = sm.sSd;
-    int* const sG = sm.sG;
-    double* const sRatio = sm.sRatio;
-    float* const sLseT = sm.sLseT;
-    float* const sLseD = sm.sLseD;
-    int* const sTok = sm.sTok;
-    float* const sU = sm.sU;
-    const int tid = threadIdx.x, K = p.K;
-    const int n = min(j0 + G - 1, K + 1) - j0 + 1;
-    const int sw = p.seg_w;
-    const int per = 2 * n * sw;
-    // Everything the group's decisions read is requested at once: the state,
-    // the split partials of every row of the group, the drafted tokens' logits,
-    // tokens and uniforms.  Their addresses depend on the group only (rows that
-    // were not streamed are loaded too and masked below), so one round trip
-    // serves them all.
-    const SeqState st0 = w.st[b];
-    float pm = -INFINITY, pd = 0.0f;
-    double ps = 0.0;
-    int pix = 0x7fffffff;
-    if (tid < per && per <= kThreads) {
-        const int pk = tid / sw, k = tid % sw, q = pk >> 1, kind = pk & 1, j = j0 + q;
-        if (k < p.nsplit && (kind == 0 || (!GREEDY && !OH && j <= K))) {
-            const long long pi = part_index(p, b, kind ? K + j : j - 1) + k;
-            pm = w.part_m[pi];
-            if (GREEDY) {
-                pix = w.part_i[pi];
-            } else {
-                ps = w.part_s[pi];
-                pd = w.part_d[pi];
-            }
-        }
+    const SeqCtl c = w.seq[b];
+    const int K = p.K;
+    Final f;
+    f.y = -1;
+    f.js = 0;
+    f.a = 0;
+    f.bad_dec = false;
+    if (c.flags & SEQ_BAD) {
+        f.kind = KIND_BAD;
+        f.L = c.Lout;
+        return f;
     }
-    float xl = 0.0f;
-    {
-        const int q = tid & 63, kind = tid >> 6, j = j0 + q;
-        if (!GREEDY && kind < 2 && q < n && j <= K && !(kind && OH))
-            xl = w.xlog[(long long)b * (2 * K + 1) + (kind ? K + j : j - 1)];
-        if (kind == 2 && q < n && j <= K) {
-            sTok[q] = p.tok[(long long)b * K + (j - 1)];
-            if (!GREEDY) sU[q] = p.u[(long long)b * (K + 1) + (j - 1)];
-        }
+    const int L1 = c.lw >> 16;
+    if (L1 == 0) { // the survival walk did not close: cannot happen (reported as SV_STATUS_INCOMPLETE)
+        f.kind = KIND_BAD;
+        f.L = -1;
+        return f;
     }
-    const float tau_b = (!GREEDY && p.derived) ? p.tau[b] : 0.0f;
-    const int flags0 = st0.flags, L0 = st0.L;
-    if (!(flags0 & (FL_ACC | FL_LEN))) return st0; // (the same in every thread)
-    for (int base = 0; base < per; base += kThreads) {
-        const int t = base + tid;
-        const int pk = t / sw, k = t % sw;
-        const int q = pk >> 1, kind = pk & 1, j = j0 + q;
-        const bool read = t < per && (kind ? (!GREEDY && !OH && draft_row_needed(flags0, L0, j, K))
-                                           : target_row_needed(flags0, L0, j, K));
-        const bool has = read && k < p.nsplit;
-        if (per > kThreads) {
-            // groups wider than one workgroup's threads (very large vocabularies)
-            const long long pi = has ? part_index(p, b, kind ? K + j : j - 1) + k : 0;
-            pm = has ? w.part_m[pi] : -INFINITY;
-            if (GREEDY) pix = has ? w.part_i[pi] : 0x7fffffff;
-            else {
-                ps = has ? w.part_s[pi] : 0.0;
-                pd = has ? w.part_d[pi] : 0.0f;
-            }
+    f.L = L1 - 1;
+    const int r = c.dead;
+    if (r <= f.L) {
+        if (w.dec[(long long)b * (K + 1) + r] == DEC_BAD) {
+            f.kind = KIND_BAD;
+            f.bad_dec = true;
+            return f;
         }
-        if (GREEDY) {
-            float v = has ? pm : -INFINITY;
-            int ix = has ? pix : 0x7fffffff;
-            seg_argmax(v, ix, sw);
-            if (read && k == 0) { sMt[q] = v; sG[q] = ix; }
-        } else {
-            const float m = has ? pm : -INFINITY;
-            const float M = seg_max(m, sw);
-            double v = (has && m != -INFINITY) ? ps * exp2_f64(((double)m - (double)M) * p.c64 - (double)pd) : 0.0;
-            v = seg_sum(v, sw);
-            if (read && k == 0) {
-                if (kind) { sMd[q] = M; sSd[q] = v; }
-                else { sMt[q] = M; sSt[q] = v; }
-            }
-        }
+        f.a = r - 1;
+        f.js = r;
+        f.kind = greedy ? KIND_GREEDY : KIND_RESID;
+    } else {
+        f.a = f.L;
+        f.js = f.L + 1;
+        f.kind = greedy ? KIND_GREEDY : KIND_BONUS;
     }
-    if (!GREEDY) {
-        // logits of the drafted tokens, kept by sv_rows: threads 0..n-1 target rows, 64..64+n-1 draft rows
-        const int q = tid & 63, kind = tid >> 6, j = j0 + q;
-        if (kind < 2 && q < n && j <= K) {
-            const bool read = kind ? draft_row_needed(flags0, L0, j, K) : target_row_needed(flags0, L0, j, K);
-            if (read) {
-                if (kind && OH) {
-                    // the one-hot draft row: logit 0 at x, -inf elsewhere (max 0, sum 1)
-                    sLd[q] = 0.0f;
-                    sMd[q] = 0.0f;
-                    sSd[q] = 1.0;
-                } else if (kind) {
-                    sLd[q] = xl;
-                } else {
-                    sLt[q] = xl;
-                }
-            }
-        }
-    }
-    __syncthreads();
-    if (!GREEDY) {
-        // per-position quantities in parallel: the acceptance ratio p(x)/q(x), and the
-        // rows' log-sum-exp when asked for (thread q handles position j0 + q)
-        const int q = tid, j = j0 + q;
-        if (q < n) {
-            const bool tread = target_row_needed(flags0, L0, j, K);
-            const bool dread = draft_row_needed(flags0, L0, j, K);
-            if (tread && dread) {
-                const float ld = sLd[q];
-                double ratio = INFINITY; // q(x) = 0
-                if (ld != -INFINITY) {
-                    const double dlt = (double)sLt[q] - (double)sMt[q], dld = (double)ld - (double)sMd[q];
-                    ratio = exp2_f64((dlt - dld) * p.c64) * (sSd[q] / sSt[q]);
-                }
-                sRatio[q] = ratio;
-            }
-            if (tread && p.lse_t) sLseT[q] = (float)((double)sMt[q] * p.invT64 + log(sSt[q]));
-            if (dread && p.lse_d && !OH) sLseD[q] = (float)((double)sMd[q] * p.invT64 + log(sSd[q]));
-        }
-    }
-    __syncthreads();
-    if (tid == 0) {
-    SeqState st = st0;
-    bool acc = (flags0 & FL_ACC) != 0;
-    bool len = (flags0 & FL_LEN) != 0;
-    for (int q = 0; q < n; ++q) {
-        const int j = j0 + q;
-        const bool dread = !GREEDY && draft_row_needed(flags0, L0, j, K);
-        st.rows += (target_row_needed(flags0, L0, j, K) ? 1 : 0) + ((dread && !OH) ? 1 : 0);
-        if (!acc && !len) continue; // rows of this group past the stop were still streamed
-        if (!GREEDY) {
-            if (writer && acc && p.lse_t) p.lse_t[(long long)b * (K + 1) + (j - 1)] = sLseT[q];
-            if (writer && dread && p.lse_d && !OH) p.lse_d[(long long)b * K + (j - 1)] = sLseD[q];
-            if (dread && p.derived && !OH) {
-                // c_j = max_v q_j(v) = 1 / Sd; S_j = S_{j-1} c_j
-                const double S = st.S / sSd[q];
-                st.S = S;
-                if (writer && p.surv) p.surv[(long long)b * K + (j - 1)] = (float)S;
-                if (len) {
-                    if (S >= (double)tau_b) {
-                        if (j == K) { st.L = K; len = false; }
-                    } else {
-                        st.L = j - 1;
-                        len = false;
-                    }
-                }
-            }
-        }
-        if (!acc) continue;
-        const bool verify = len || st.L >= j; // open length walk means S_j >= tau, so L >= j
-        if (verify) {
-            const int x = sTok[q];
-            if (x < 0 || x >= p.V) {
-                st.kind = KIND_BAD;
-                st.a = 0;
-                acc = false;
-                if (writer) or_status(&w.ctl[CTL_STATUS], SV_STATUS_BAD_INPUT);
-            } else if (GREEDY) {
-                if (x == sG[q]) {
-                    st.a = j;
-                } else {
-                    st.kind = KIND_GREEDY;
-                    st.y = sG[q];
-                    acc = false;
-                }
-            } else {
-                const double ratio = sRatio[q];
-                const double uj = (double)sU[q];
-                if (uj < ratio) {
-                    st.a = j;
-                } else {
-                    st.kind = KIND_RESID;
-                    st.js = j;
-                    st.Mt = sMt[q]; st.St = sSt[q]; st.Md = sMd[q]; st.Sd = sSd[q];
-                    acc = false;
-                }
-            }
-        } else {
-            // L == j - 1: the final token comes from target row j
-            if (GREEDY) {
-                st.kind = KIND_GREEDY;
-                st.y = sG[q];
-            } else {
-                st.kind = KIND_BONUS;
-                st.js = j;
-                st.Mt = sMt[q]; st.St = sSt[q];
-            }
-            acc = false;
-        }
-    }
-    st.flags = (acc ? FL_ACC : 0) | (len ? FL_LEN : 0);
-    sm.st = st;
-    }
-    __syncthreads();
-    return sm.st;
-}
-
-// One workgroup per sequence.
-template <int DT, bool GREEDY, int MODE>
-__global__ __launch_bounds__(kThreads) void sv_decide_kernel(Params p, Work w, int j0, int G)
-{
-    __shared__ DecideSmem sm;
-    const int b = (int)blockIdx.x;
-    const SeqState st = decide_group<DT, GREEDY, MODE>(p, w, b, j0, G, true, sm);
-    if (threadIdx.x == 0) {
-        w.st[b] = st;
-        w.live[b] = st.flags ? (((st.L + 1) << 2) | st.flags) : 0;
-    }
+    if (greedy) f.y = w.row_g[row_index(p, b, f.js - 1)];
+    return f;
 }
 
 // ---------------------------------------------------------------- final draw
@@ -1115,31 +1106,40 @@ struct Seg {
 };
 constexpr int kSegStride = 64; // segment sums stored per split
 
-// The rows' 1/S enter the fp32 masses as two fp32 parts (hi + lo, ~2^-48
-// relative): a single fp32 rounding would scale every p (or q) of the row by the
-// same factor, an error that does not cancel in p - q and is large relative to
-// the residual mass when the rows are nearly equal.
+// Token masses of the final draw.  p_v = 2^((l_v - Mt) c) / St with 1/St in two
+// fp32 parts (~2^-48 relative); a replacement takes r_v = max(0, p_v - q_v) as
+// p_v (1 - 2^-D_v) with D_v = log2(p_v / q_v) = c ((lt_v - ld_v) - (Mt - Md)) +
+// log2(Sd / St): the logit difference is exact (a two-sum for fp32 logits;
+// bf16 logits differ exactly in fp32), Mt - Md and log2(Sd / St) come from fp64
+// in two fp32 parts, and 1 - 2^-D comes from its series when |D| < 1/4, so r_v
+// keeps its relative accuracy when p and q nearly agree (no cancellation of
+// two separately rounded masses).
 struct DrawCtx {
-    float Mt, Md, iSt_hi, iSt_lo, iSd_hi, iSd_lo, c_hi, c_lo;
-    double iSt, iSd, c64;
+    float Mt, c_hi, c_lo, iSt_hi, iSt_lo;
+    float dM_hi, dM_lo, k_hi, k_lo, c32;
+    double Mt64, iSt64, dM64, k64, c64;
 };
 
 __device__ __forceinline__ float scale2(float e, float hi, float lo) { return fmaf(e, hi, e * lo); }
 
-__device__ __forceinline__ DrawCtx make_ctx(const SeqState& st, const Params& p)
+__device__ __forceinline__ DrawCtx make_ctx(float Mt, double St, float Md, double Sd, bool resid, const Params& p)
 {
     DrawCtx c;
-    c.Mt = st.Mt;
-    c.Md = st.Md;
-    c.iSt = 1.0 / st.St;
-    c.iSd = st.Sd > 0.0 ? 1.0 / st.Sd : 0.0;
-    c.iSt_hi = (float)c.iSt;
-    c.iSt_lo = (float)(c.iSt - (double)c.iSt_hi);
-    c.iSd_hi = (float)c.iSd;
-    c.iSd_lo = (float)(c.iSd - (double)c.iSd_hi);
+    c.Mt = Mt;
+    c.Mt64 = (double)Mt;
+    c.iSt64 = 1.0 / St;
+    c.iSt_hi = (float)c.iSt64;
+    c.iSt_lo = (float)(c.iSt64 - (double)c.iSt_hi);
     c.c_hi = p.c_hi;
     c.c_lo = p.c_lo;
+    c.c32 = p.c32;
     c.c64 = p.c64;
+    c.dM64 = resid ? (double)Mt - (double)Md : 0.0;
+    c.k64 = resid ? log2(Sd / St) : 0.0;
+    c.dM_hi = (float)c.dM64;
+    c.dM_lo = (float)(c.dM64 - (double)c.dM_hi);
+    c.k_hi = (float)c.k64;
+    c.k_lo = (float)(c.k64 - (double)c.k_hi);
     return c;
 }
 
@@ -1157,31 +1157,118 @@ __device__ __forceinline__ double uniform_f64(double v)
 __device__ __forceinline__ DrawCtx uniform_ctx(const DrawCtx& c)
 {
     DrawCtx u;
-    u.Mt = uniform_f32(c.Mt); u.Md = uniform_f32(c.Md);
+    u.Mt = uniform_f32(c.Mt); u.c_hi = uniform_f32(c.c_hi); u.c_lo = uniform_f32(c.c_lo);
     u.iSt_hi = uniform_f32(c.iSt_hi); u.iSt_lo = uniform_f32(c.iSt_lo);
-    u.iSd_hi = uniform_f32(c.iSd_hi); u.iSd_lo = uniform_f32(c.iSd_lo);
-    u.c_hi = uniform_f32(c.c_hi); u.c_lo = uniform_f32(c.c_lo);
-    u.iSt = uniform_f64(c.iSt); u.iSd = uniform_f64(c.iSd); u.c64 = uniform_f64(c.c64);
+    u.dM_hi = uniform_f32(c.dM_hi); u.dM_lo = uniform_f32(c.dM_lo);
+    u.k_hi = uniform_f32(c.k_hi); u.k_lo = uniform_f32(c.k_lo); u.c32 = uniform_f32(c.c32);
+    u.Mt64 = uniform_f64(c.Mt64); u.iSt64 = uniform_f64(c.iSt64); u.dM64 = uniform_f64(c.dM64);
+    u.k64 = uniform_f64(c.k64); u.c64 = uniform_f64(c.c64);
     return u;
 }
 
-__device__ __forceinline__ double mass_f64(float lt, float ld, const DrawCtx& c, bool resid)
+__device__ __forceinline__ float p_mass32(float lt, const DrawCtx& c)
 {
-    const double pd = exp2_f64(((double)lt - (double)c.Mt) * c.c64) * c.iSt;
-    const double qd = resid ? exp2_f64(((double)ld - (double)c.Md) * c.c64) * c.iSd : 0.0;
-    return pd > qd ? pd - qd : 0.0;
+    return scale2(scaled_exp2(lt, c.Mt, c.c_hi, c.c_lo), c.iSt_hi, c.iSt_lo);
 }
 
-// Mass of one token under the final draw: max(0, p - q) for a replacement,
-// p for a bonus.  fp32 first; masses whose p or q exceeds 2^-9 are evaluated
-// in fp64 (at most 2^10 tokens of a row pair qualify).  Below that, the fp32
-// value carries a few 1e-8 relative error, independent from token to token.
-__device__ __forceinline__ double draw_mass(float lt, float ld, const DrawCtx& c, bool resid)
+// 1 - 2^-D: for |D| < 1/4 from the series of 1 - e^-x (x = D ln 2, to the x^6
+// term: truncation below 4e-8 relative), else 1 - v_exp_f32(-D) (the
+// difference is then at least 0.159, so exp's ulp costs < 4e-7 relative).
+__device__ __forceinline__ float one_minus_exp2_neg(float D)
 {
-    const float pf = scale2(scaled_exp2(lt, c.Mt, c.c_hi, c.c_lo), c.iSt_hi, c.iSt_lo);
-    const float qf = resid ? scale2(scaled_exp2(ld, c.Md, c.c_hi, c.c_lo), c.iSd_hi, c.iSd_lo) : 0.0f;
-    if (fmaxf(pf, qf) > 0x1p-9f) return mass_f64(lt, ld, c, resid);
-    return (double)fmaxf(pf - qf, 0.0f);
+    const float x = D * 0.693147181f;
+    float s = fmaf(x, -1.0f / 720.0f, 1.0f / 120.0f);
+    s = fmaf(s, x, -1.0f / 24.0f);
+    s = fmaf(s, x, 1.0f / 6.0f);
+    s = fmaf(s, x, -0.5f);
+    s = fmaf(s, x, 1.0f);
+    return fabsf(D) < 0.25f ? s * x : 1.0f - __builtin_amdgcn_exp2f(-D);
+}
+
+// Residual mass of one token in fp32 (see DrawCtx).  -inf logits: q_v = 0
+// gives D = +inf and r_v = p_v; p_v = 0 gives 0 (a NaN D is dropped by fmaxf).
+template <int DT>
+__device__ __forceinline__ float resid_mass32(float lt, float ld, const DrawCtx& c)
+{
+    const float pf = p_mass32(lt, c);
+    float u;
+    if (DT == SV_BF16) {
+        u = ((lt - ld) - c.dM_hi) - c.dM_lo;
+    } else {
+        const float lq = fmaxf(ld, -0x1p127f); // keeps the two-sum finite when q_v = 0
+        const float s = lt - lq;
+        const float bb = s - lt;
+        const float e = (lt - (s - bb)) - (lq + bb);
+        u = ((s - c.dM_hi) + e) - c.dM_lo;
+    }
+    const float D = fmaf(u, c.c32, c.k_hi) + c.k_lo;
+    return pf * fmaxf(one_minus_exp2_neg(D), 0.0f);
+}
+
+template <int DT>
+__device__ __forceinline__ float draw_mass32(float lt, float ld, const DrawCtx& c, bool resid)
+{
+    return resid ? resid_mass32<DT>(lt, ld, c) : p_mass32(lt, c);
+}
+
+// The residual mass of one token with the two sums that renormalise the draft
+// row against the target row (see the renormalisation at sv_draw): qa = q_v
+// on the residual's support (where p > q) and kap = p_v - q_v (signed, over
+// every token), both as p_v times a factor of 2^-D.  bad: the token's q_v
+// exceeds p_v by more than 2^120 (a target logit of -inf where the draft has
+// mass), where kap cannot be formed this way.
+template <int DT>
+__device__ __forceinline__ void resid_parts32(float lt, float ld, const DrawCtx& c, float& r, float& qa, float& kap,
+                                              float& pp, bool& bad)
+{
+    const float pf = p_mass32(lt, c);
+    float u;
+    if (DT == SV_BF16) {
+        u = ((lt - ld) - c.dM_hi) - c.dM_lo;
+    } else {
+        const float lq = fmaxf(ld, -0x1p127f);
+        const float s = lt - lq;
+        const float bb = s - lt;
+        const float e = (lt - (s - bb)) - (lq + bb);
+        u = ((s - c.dM_hi) + e) - c.dM_lo;
+    }
+    const float D = fmaf(u, c.c32, c.k_hi) + c.k_lo;
+    const bool ok = D >= -120.0f;
+    const float om = one_minus_exp2_neg(ok ? D : -120.0f);
+    r = pf * fmaxf(om, 0.0f);
+    qa = om > 0.0f ? pf - r : 0.0f;
+    kap = ok ? pf * om : 0.0f;
+    pp = pf;
+    bad = !ok && ld > -INFINITY;
+}
+
+// The same mass in fp64 (the reported probability of the drawn token); qa:
+// q_v where the residual is positive, else 0.
+__device__ __forceinline__ double draw_mass64(float lt, float ld, const DrawCtx& c, bool resid, double& qa)
+{
+    const double pd = exp2_f64(((double)lt - c.Mt64) * c.c64) * c.iSt64;
+    qa = 0.0;
+    if (!resid || !(ld > -INFINITY)) return pd;
+    const double D = (((double)lt - (double)ld) - c.dM64) * c.c64 + c.k64;
+    double om;
+    if (fabs(D) < 0.0625) {
+        // 1 - e^-x = x sum_{m=0}^{8} (-x)^m / (m+1)!, |x| < 0.044: truncation below 1e-18
+        const double x = D * 0.69314718055994530942, y = -x;
+        double h = 1.0 / 362880.0;
+        h = fma(h, y, 1.0 / 40320.0);
+        h = fma(h, y, 1.0 / 5040.0);
+        h = fma(h, y, 1.0 / 720.0);
+        h = fma(h, y, 1.0 / 120.0);
+        h = fma(h, y, 1.0 / 24.0);
+        h = fma(h, y, 1.0 / 6.0);
+        h = fma(h, y, 0.5);
+        h = fma(h, y, 1.0);
+        om = x * h;
+    } else {
+        om = 1.0 - exp2_f64(-D);
+    }
+    if (om > 0.0) qa = pd * (1.0 - om);
+    return pd * fmax(om, 0.0);
 }
 
 // Inclusive prefix sum over the 64 lanes of a wavefront (fixed order).
@@ -1195,37 +1282,20 @@ __device__ __forceinline__ double wave_incl_scan(double v, int lane)
     return v;
 }
 
-// Mass of a run of RUN consecutive tokens, in token order.  The fast path is
-// branch-free fp32 per token, summed in fp64; a run that holds a token whose p
-// or q exceeds 2^-9 is summed again with draw_mass (fp64 for those tokens).
-// Both kernels that need a run's mass call this, so the sums agree bit for bit.
-template <int RUN>
-__device__ __forceinline__ double run_mass(const float (&lt)[RUN], const float (&ld)[RUN], const DrawCtx& c, bool resid,
-                                           bool& slow)
+// Mass of a run of RUN consecutive tokens: per-token fp32 masses summed
+// pairwise in fp32 (at most 3 roundings deep), then widened.  Every kernel
+// that needs a run's mass calls this, so the sums agree bit for bit.
+template <int DT, int RUN>
+__device__ __forceinline__ double run_mass(const float (&lt)[RUN], const float (&ld)[RUN], const DrawCtx& c, bool resid)
 {
-    // fmaxf(pf - qf, 0) equals (pf > qf ? pf - qf : 0) for these finite
-    // values; the run is tested once, on its largest p or q
-    double acc = 0.0;
-    float big = 0.0f;
+    float m[RUN];
 #pragma unroll
-    for (int i = 0; i < RUN; ++i) {
-        const float pf = scale2(scaled_exp2(lt[i], c.Mt, c.c_hi, c.c_lo), c.iSt_hi, c.iSt_lo);
-        const float qf = resid ? scale2(scaled_exp2(ld[i], c.Md, c.c_hi, c.c_lo), c.iSd_hi, c.iSd_lo) : 0.0f;
-        big = fmaxf(big, fmaxf(pf, qf));
-        acc += (double)fmaxf(pf - qf, 0.0f);
-    }
-    slow = big > 0x1p-9f;
-    return acc;
-}
-
-template <int RUN>
-__device__ __forceinline__ double run_mass_exact(const float (&lt)[RUN], const float (&ld)[RUN], const DrawCtx& c,
-                                                 bool resid)
-{
-    double acc = 0.0;
+    for (int i = 0; i < RUN; ++i) m[i] = draw_mass32<DT>(lt[i], ld[i], c, resid);
 #pragma unroll
-    for (int i = 0; i < RUN; ++i) acc += draw_mass(lt[i], ld[i], c, resid);
-    return acc;
+    for (int w = 1; w < RUN; w <<= 1)
+#pragma unroll
+        for (int i = 0; i + w < RUN; i += 2 * w) m[i] += m[i + w];
+    return (double)m[0];
 }
 
 // Segment sums of one split (all 256 threads): lane run sums of RUN tokens,
@@ -1244,60 +1314,133 @@ __device__ __forceinline__ void split_segments(const Chunk<DT>& tc, const Chunk<
             lt[i] = tc.get(k * S::RUN + i);
             ld[i] = resid ? dc.get(k * S::RUN + i) : 0.0f;
         }
-        bool slow;
-        double r = run_mass<S::RUN>(lt, ld, c, resid, slow);
-        if (slow) r = run_mass_exact<S::RUN>(lt, ld, c, resid); // rare: a large p or q in the run
+        const double r = run_mass<DT, S::RUN>(lt, ld, c, resid);
         const double incl = wave_incl_scan(r, lane);
         if (lane == 63) seg_out[k * kWaves + wv] = incl;
     }
 }
 
-// One workgroup per (sequence, split, half of the split): first the decisions
-// of the last position group (positions j0 .. j0+G-1), taken by each of the
-// sequence's workgroups from the group's partials (the one of split 0, half 0
-// writes the outputs and w.fin), then, if they end in a rejection, the
-// residual mass of each of the half's segments (w.seg).  Taking the last
-// decisions here saves a launch and its drain.  Halves (32 tokens per lane) keep
-// the workgroups short and balance the compute-bound pass (two exponentials
-// per token) better than whole splits; quarters and eighths measured slower.
+// ---------------------------------------------------------------- sv_resid
+//
+// Renormalisation of nearly equal rows.  Every token's residual uses the log
+// ratio of the two row sums, log2(Sd / St), from the row statistics; their
+// errors (a few 1e-8, from fp32 exponents and run sums) are independent, so
+// the ratio is off by a few 1e-8 and every r_v = p_v (1 - 2^-D_v) by about
+// q_v times that -- negligible against Z unless the rows nearly agree (Z ~
+// 1e-3 and below).  For such a row pair the residual pass also sums
+// kap = sum_v (p_v - q_v) over all tokens and P = sum_v p_v, each term formed
+// from the exact logit difference (so kap's error is ~1e-7 of sum |p - q| =
+// 2Z, not of 1), and qa = q_v over the residual's support per segment.  Then
+// q is rescaled to the same total as p: q_v -> q_v F, F = P / (P - kap), and
+// to first order r_v -> r_v - (F - 1) q_v on the support, Z -> (Z - (F - 1)
+// QA) / P.  Which row pairs: those whose rejected token has p(x)/q(x) within
+// 1/8 of 1 (nearly equal rows give ratios near 1 for every token); the test
+// reads only stored records, so both kernels take it identically.
+constexpr int kKpStride = 4; // (kap, P, bad, -) per half split
+
+__device__ __forceinline__ bool near_equal_rows(const Params& p, const Work& w, int b, int js)
+{
+    const long long rt = row_index(p, b, js - 1), rd = row_index(p, b, p.K + js);
+    const float xd = w.xlog[rd];
+    if (xd == -INFINITY) return false;
+    const double ratio =
+        exp2_f64((((double)w.xlog[rt] - (double)w.row_m[rt]) - ((double)xd - (double)w.row_m[rd])) * p.c64) *
+        (w.row_s[rd] / w.row_s[rt]);
+    return fabs(ratio - 1.0) < 0.125;
+}
+
+// One workgroup per (sequence, split, half of the split): if the sequence's
+// walk ended in a rejection at position js, the residual mass of each of the
+// half's segments of row pair js (w.seg), and for nearly equal rows the
+// renormalisation sums (w.segq, w.kp).  Halves (32 tokens per lane) keep the
+// workgroups short and balance the compute-bound pass (two exponentials per
+// token) better than whole splits.
 template <int DT, bool VEC, int MODE>
-__global__ __launch_bounds__(kThreads) void sv_resid_kernel(Params p, Work w, int j0, int G)
+__global__ __launch_bounds__(kThreads) void sv_resid_kernel(Params p, Work w)
 {
     static_assert((MODE & MODE_ONEHOT) == 0, "one-hot drafts have no residual pass");
     constexpr bool PK = (MODE & MODE_PACKED) != 0;
     using S = Seg<DT>;
     constexpr int NL = Part<DT>::NL, QSEG = NL * kWaves;
-    __shared__ double s_seg[QSEG];
-    __shared__ DecideSmem sm;
+    __shared__ double s_seg[QSEG], s_segq[QSEG];
+    __shared__ double s_red[kWaves];
     const int q = (int)(blockIdx.x % kParts);
     const int split = (int)((blockIdx.x / kParts) % p.nsplit);
     const int b = (int)(blockIdx.x / kParts / p.nsplit);
-    const bool writer = split == 0 && q == 0;
-    const SeqState st = decide_group<DT, false, 0>(p, w, b, j0, G, writer, sm);
-    if (writer && threadIdx.x == 0) w.fin[b] = st;
-    if (st.kind != KIND_RESID) return;
-    const DrawCtx c = uniform_ctx(make_ctx(st, p));
+    const Final f = final_state(p, w, b, false);
+    if (f.kind != KIND_RESID) return;
+    const int K = p.K;
+    const long long rt = row_index(p, b, f.js - 1), rd = row_index(p, b, K + f.js);
+    const DrawCtx c = uniform_ctx(make_ctx(w.row_m[rt], w.row_s[rt], w.row_m[rd], w.row_s[rd], true, p));
+    const bool fine = near_equal_rows(p, w, b, f.js);
     const int t = (int)threadIdx.x, lane = t & 63, wv = t >> 6;
     Part<DT> tc, dc;
-    tc.template load<VEC>(seq_row<DT, PK>(p.t, p.toff, p.tbs, p.trs, b, st.js - 1), split * kSplit, p.V, t, q);
-    dc.template load<VEC>(seq_row<DT, PK>(p.d, p.doff, p.dbs, p.drs, b, st.js - 1), split * kSplit, p.V, t, q);
+    tc.template load<VEC>(seq_row<DT, PK>(p.t, p.toff, p.tbs, p.trs, b, f.js - 1), split * kSplit, p.V, t, q);
+    dc.template load<VEC>(seq_row<DT, PK>(p.d, p.doff, p.dbs, p.drs, b, f.js - 1), split * kSplit, p.V, t, q);
+    const long long so = ((long long)b * p.nsplit + split) * kSegStride + q * QSEG;
+    if (!fine) {
+#pragma unroll
+        for (int k = 0; k < NL; ++k) {
+            float lt[S::RUN], ld[S::RUN];
+#pragma unroll
+            for (int i = 0; i < S::RUN; ++i) {
+                lt[i] = tc.get(k * S::RUN + i);
+                ld[i] = dc.get(k * S::RUN + i);
+            }
+            const double r = run_mass<DT, S::RUN>(lt, ld, c, true);
+            const double incl = wave_incl_scan(r, lane);
+            if (lane == 63) s_seg[k * kWaves + wv] = incl;
+        }
+        __syncthreads();
+        if (t < QSEG) w.seg[so + t] = s_seg[t];
+        return;
+    }
+    double kap = 0.0, pp = 0.0;
+    bool bad = false;
 #pragma unroll
     for (int k = 0; k < NL; ++k) {
-        float lt[S::RUN], ld[S::RUN];
+        float r[S::RUN], qa[S::RUN], kp[S::RUN], pv[S::RUN];
 #pragma unroll
         for (int i = 0; i < S::RUN; ++i) {
-            lt[i] = tc.get(k * S::RUN + i);
-            ld[i] = dc.get(k * S::RUN + i);
+            bool bi;
+            resid_parts32<DT>(tc.get(k * S::RUN + i), dc.get(k * S::RUN + i), c, r[i], qa[i], kp[i], pv[i], bi);
+            bad |= bi;
         }
-        bool slow;
-        double r = run_mass<S::RUN>(lt, ld, c, true, slow);
-        if (slow) r = run_mass_exact<S::RUN>(lt, ld, c, true); // rare: a large p or q in the run
-        const double incl = wave_incl_scan(r, lane);
-        if (lane == 63) s_seg[k * kWaves + wv] = incl;
+        // pairwise in fp32 (the residual in the same order as run_mass)
+#pragma unroll
+        for (int h = 1; h < S::RUN; h <<= 1)
+#pragma unroll
+            for (int i = 0; i + h < S::RUN; i += 2 * h) {
+                r[i] += r[i + h];
+                qa[i] += qa[i + h];
+                kp[i] += kp[i + h];
+                pv[i] += pv[i + h];
+            }
+        kap += (double)kp[0];
+        pp += (double)pv[0];
+        const double incl = wave_incl_scan((double)r[0], lane);
+        const double inclq = wave_incl_scan((double)qa[0], lane);
+        if (lane == 63) {
+            s_seg[k * kWaves + wv] = incl;
+            s_segq[k * kWaves + wv] = inclq;
+        }
     }
-    __syncthreads();
-    if (t < QSEG) w.seg[((long long)b * p.nsplit + split) * kSegStride + q * QSEG + t] = s_seg[t];
+    const bool anybad = __syncthreads_or(bad);
+    kap = block_sum(kap, s_red, t);
+    pp = block_sum(pp, s_red, t);
+    if (t < QSEG) {
+        w.seg[so + t] = s_seg[t];
+        w.segq[so + t] = s_segq[t];
+    }
+    if (t == 0) {
+        double* kq = w.kp + (((long long)b * p.nsplit + split) * kParts + q) * kKpStride;
+        kq[0] = kap;
+        kq[1] = pp;
+        kq[2] = anybad ? 1.0 : 0.0;
+    }
 }
+
+// ---------------------------------------------------------------- sv_draw
 
 // First lane whose inclusive prefix exceeds w (lanes < n), as (lane, w minus
 // the exclusive prefix of that lane); lane -1 if none.  All lanes take part.
@@ -1322,31 +1465,51 @@ __device__ __forceinline__ int wave_last_positive(double v, int n)
     return pos ? 63 - __clzll(pos) : -1;
 }
 
-// sts: the states after the last group (w.fin when sv_resid took the last
-// decisions, else w.st).
-template <int DT, bool VEC, int MODE>
-__global__ __launch_bounds__(kThreads) void sv_draw_kernel(Params p, Work w, const SeqState* __restrict__ sts)
+// Mass of split k of target row js under p, from the row statistics' partials.
+__device__ __forceinline__ double split_p_mass(const Params& p, const Work& w, int b, int js, int k, float Mt, double St)
+{
+    const long long pb = part_index(p, b, js - 1) + k;
+    const float mk = w.part_m[pb];
+    if (mk == -INFINITY) return 0.0;
+    return w.part_s[pb] * exp2_f64(((double)mk - (double)Mt) * p.c64 - (double)w.part_d[pb]) / St;
+}
+
+// One workgroup per sequence: the final draw, the emitted block and the
+// diagnostics.  The last workgroup to finish reports the call's status bits.
+template <int DT, bool VEC, bool GREEDY, int MODE>
+__global__ __launch_bounds__(kThreads) void sv_draw_kernel(Params p, Work w)
 {
     constexpr bool OH = (MODE & MODE_ONEHOT) != 0, PK = (MODE & MODE_PACKED) != 0;
     using S = Seg<DT>;
     extern __shared__ double s_all[];  // [nsplit][SEGS] residual segment sums of the sequence
     __shared__ double s_bonus[S::SEGS]; // segment sums of the bonus draw's split
-    __shared__ double s_wrel, s_Z, s_my;
+    __shared__ double s_wrel, s_Z, s_my, s_F1, s_P;
     __shared__ int s_split, s_resid, s_y;
+    __shared__ double s_cnt[kWaves];
     const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
     const int K = p.K;
+    const long long R = 2LL * K + 1, rb = (long long)b * R;
     // requested together with the state: the final draw's uniform and the
     // drafted tokens this thread copies to the output
     const float uf32 = (p.u == nullptr) ? 0.0f : p.u[(long long)b * (K + 1) + K];
     const int tok0 = tid < K ? p.tok[(long long)b * K + tid] : -1;
-    const SeqState st = sts[b];
-    int kind = st.kind;
-    int a = st.a;
+    const Final f = final_state(p, w, b, GREEDY);
+    int kind = f.kind;
+    const int a = f.a;
     int y = -1;
     float zrep = NAN, py = NAN;
 
     if (kind == KIND_RESID || kind == KIND_BONUS) {
+        const int js = f.js;
+        const float Mt = w.row_m[rb + js - 1];
+        const double St = w.row_s[rb + js - 1];
+        float Md = 0.0f;
+        double Sd = 1.0; // one-hot draft row: max 0, sum 1
+        // nearly equal rows: the residual is renormalised (see sv_resid)
+        const bool fine = kind == KIND_RESID && !OH && near_equal_rows(p, w, b, js);
         if (kind == KIND_RESID && !OH) {
+            Md = w.row_m[rb + K + js];
+            Sd = w.row_s[rb + K + js];
             // every segment sum of the sequence at once (one round trip): the
             // split totals and the search inside the chosen split both read LDS
             const double* sg = w.seg + (long long)b * p.nsplit * kSegStride;
@@ -1357,38 +1520,49 @@ __global__ __launch_bounds__(kThreads) void sv_draw_kernel(Params p, Work w, con
         // 1. the split holding the draw point (wave 0, lane k = split k)
         if (tid < 64) {
             bool resid = kind == KIND_RESID;
-            double m = 0.0;
+            double m = 0.0, F1 = 0.0, P = 1.0;
+            if (fine) {
+                // F - 1 = kap / (P - kap) from the half splits' sums (fixed order)
+                const double* kq = w.kp + (long long)b * p.nsplit * kParts * kKpStride;
+                double kv = 0.0, pv = 0.0;
+                bool bad = false;
+                for (int i = lane; i < p.nsplit * kParts; i += 64) {
+                    kv += kq[i * kKpStride];
+                    pv += kq[i * kKpStride + 1];
+                    bad |= kq[i * kKpStride + 2] != 0.0;
+                }
+                const double kap = wave_sum(kv);
+                P = wave_sum(pv);
+                F1 = (__ballot(bad) || !(P > kap)) ? 0.0 : kap / (P - kap);
+            }
             if (resid && !OH && lane < p.nsplit) {
                 // residual mass of split `lane`: its segments summed in order
 #pragma unroll 8
                 for (int g = 0; g < S::SEGS; ++g) m += s_all[lane * S::SEGS + g];
+                if (fine) {
+                    const double* sq = w.segq + ((long long)b * p.nsplit + lane) * kSegStride;
+                    double mq = 0.0;
+#pragma unroll 8
+                    for (int g = 0; g < S::SEGS; ++g) mq += sq[g];
+                    m = fmax(m - F1 * mq, 0.0);
+                }
             }
             if (resid && OH) {
                 // one-hot drafts (no residual pass): the residual is p without
                 // x, so split `lane` carries its mass of p, less p(x) in the
                 // split holding x
-                const int x = p.tok[(long long)b * K + (st.js - 1)];
-                const void* trow = seq_row<DT, PK>(p.t, p.toff, p.tbs, p.trs, b, st.js - 1);
-                const double px =
-                    exp2_f64(((double)load_one<DT>(trow, x) - (double)st.Mt) * p.c64) / st.St;
+                const int x = p.tok[(long long)b * K + (js - 1)];
+                const void* trow = seq_row<DT, PK>(p.t, p.toff, p.tbs, p.trs, b, js - 1);
+                const double px = exp2_f64(((double)load_one<DT>(trow, x) - (double)Mt) * p.c64) / St;
                 if (lane < p.nsplit) {
-                    const long long pb = part_index(p, b, st.js - 1) + lane;
-                    const float mk = w.part_m[pb];
-                    if (mk != -INFINITY)
-                        m = w.part_s[pb] * exp2_f64(((double)mk - (double)st.Mt) * p.c64 - (double)w.part_d[pb]) / st.St;
+                    m = split_p_mass(p, w, b, js, lane, Mt, St);
                     if (x / kSplit == lane) m = fmax(m - px, 0.0);
                 }
             }
             const double Z = __shfl(wave_incl_scan(m, lane), p.nsplit - 1);
             if (resid && !(Z > 0.0)) resid = false; // cannot happen in exact arithmetic after a rejection
             if (!resid) {
-                m = 0.0;
-                if (lane < p.nsplit) {
-                    const long long pb = part_index(p, b, st.js - 1) + lane;
-                    const float mk = w.part_m[pb];
-                    if (mk != -INFINITY)
-                        m = w.part_s[pb] * exp2_f64(((double)mk - (double)st.Mt) * p.c64 - (double)w.part_d[pb]) / st.St;
-                }
+                m = lane < p.nsplit ? split_p_mass(p, w, b, js, lane, Mt, St) : 0.0;
             }
             const double uf = (double)uf32;
             double wrel;
@@ -1402,15 +1576,17 @@ __global__ __launch_bounds__(kThreads) void sv_draw_kernel(Params p, Work w, con
                 s_wrel = wrel;
                 s_resid = resid ? 1 : 0;
                 s_Z = kind == KIND_RESID ? (resid ? Z : 0.0) : 1.0;
+                s_F1 = resid ? F1 : 0.0;
+                s_P = (fine && resid) ? P : 1.0; // the target row's own total
             }
         }
         __syncthreads();
         const bool resid = s_resid != 0;
         const int ks = s_split;
-        const DrawCtx c = make_ctx(st, p);
-        const void* trow = seq_row<DT, PK>(p.t, p.toff, p.tbs, p.trs, b, st.js - 1);
-        const void* drow = (resid && !OH) ? seq_row<DT, PK>(p.d, p.doff, p.dbs, p.drs, b, st.js - 1) : nullptr;
-        const int xone = (resid && OH) ? p.tok[(long long)b * K + (st.js - 1)] : -1; // one-hot draft token
+        const DrawCtx c = make_ctx(Mt, St, Md, Sd, resid, p);
+        const void* trow = seq_row<DT, PK>(p.t, p.toff, p.tbs, p.trs, b, js - 1);
+        const void* drow = (resid && !OH) ? seq_row<DT, PK>(p.d, p.doff, p.dbs, p.drs, b, js - 1) : nullptr;
+        const int xone = (resid && OH) ? p.tok[(long long)b * K + (js - 1)] : -1; // one-hot draft token
 
         // 2. segment sums of that split: stored by sv_resid for a replacement
         //    (already in LDS), computed here for a bonus draw and for a
@@ -1438,11 +1614,15 @@ __global__ __launch_bounds__(kThreads) void sv_draw_kernel(Params p, Work w, con
 
         // 3. segment, lane and token (wave 0)
         if (tid < 64) {
-            const double wrel = s_wrel;
+            const double wrel = s_wrel, F1 = s_F1;
+            const bool corr = fine && resid;
+            double sv = lane < S::SEGS ? s_seg[lane] : 0.0;
+            if (corr && lane < S::SEGS)
+                sv = fmax(sv - F1 * w.segq[((long long)b * p.nsplit + ks) * kSegStride + lane], 0.0);
             double wseg = INFINITY;
-            int g = wrel == INFINITY ? -1 : wave_select(lane < S::SEGS ? s_seg[lane] : 0.0, S::SEGS, wrel, wseg);
+            int g = wrel == INFINITY ? -1 : wave_select(sv, S::SEGS, wrel, wseg);
             if (g < 0) {
-                g = max(wave_last_positive(lane < S::SEGS ? s_seg[lane] : 0.0, S::SEGS), 0);
+                g = max(wave_last_positive(sv, S::SEGS), 0);
                 wseg = INFINITY;
             }
             const int i0 = ks * kSplit + g * S::SEGLEN + lane * S::RUN;
@@ -1454,24 +1634,33 @@ __global__ __launch_bounds__(kThreads) void sv_draw_kernel(Params p, Work w, con
                             ? (OH ? (i0 + i == xone ? 0.0f : -INFINITY) : load_one<DT>(drow, i0 + i))
                             : -INFINITY;
             }
-            bool slow;
-            double r = run_mass<S::RUN>(lt, ld, c, resid, slow);
-            if (slow) r = run_mass_exact<S::RUN>(lt, ld, c, resid);
+            double r;
             // per-token masses with the same arithmetic as the run sum, for the walk
             double m[S::RUN];
             int lastpos = -1;
+            if (corr) {
+                float rr[S::RUN], qq[S::RUN], kk, pp;
+                bool bb;
 #pragma unroll
-            for (int i = 0; i < S::RUN; ++i) {
-                if (slow) {
-                    m[i] = draw_mass(lt[i], ld[i], c, resid);
-                } else {
-                    const float pf = scale2(scaled_exp2(lt[i], c.Mt, c.c_hi, c.c_lo), c.iSt_hi, c.iSt_lo);
-                    const float qf =
-                        resid ? scale2(scaled_exp2(ld[i], c.Md, c.c_hi, c.c_lo), c.iSd_hi, c.iSd_lo) : 0.0f;
-                    m[i] = (double)fmaxf(pf - qf, 0.0f);
-                }
-                if (m[i] > 0.0) lastpos = i0 + i;
+                for (int i = 0; i < S::RUN; ++i) resid_parts32<DT>(lt[i], ld[i], c, rr[i], qq[i], kk, pp, bb);
+#pragma unroll
+                for (int i = 0; i < S::RUN; ++i) m[i] = fmax((double)rr[i] - F1 * (double)qq[i], 0.0);
+#pragma unroll
+                for (int h = 1; h < S::RUN; h <<= 1)
+#pragma unroll
+                    for (int i = 0; i + h < S::RUN; i += 2 * h) {
+                        rr[i] += rr[i + h];
+                        qq[i] += qq[i + h];
+                    }
+                r = fmax((double)rr[0] - F1 * (double)qq[0], 0.0);
+            } else {
+                r = run_mass<DT, S::RUN>(lt, ld, c, resid);
+#pragma unroll
+                for (int i = 0; i < S::RUN; ++i) m[i] = (double)draw_mass32<DT>(lt[i], ld[i], c, resid);
             }
+#pragma unroll
+            for (int i = 0; i < S::RUN; ++i)
+                if (m[i] > 0.0) lastpos = i0 + i;
             double wl;
             int l = wseg == INFINITY ? -1 : wave_select(r, 64, wseg, wl);
             bool walk = l >= 0;
@@ -1494,37 +1683,85 @@ __global__ __launch_bounds__(kThreads) void sv_draw_kernel(Params p, Work w, con
 #pragma unroll
                 for (int i = 1; i < S::RUN; ++i)
                     if (i0 + i == yy) { lty = lt[i]; ldy = ld[i]; }
-                s_my = mass_f64(lty, resid ? ldy : 0.0f, c, resid);
+                double qy;
+                s_my = draw_mass64(lty, ldy, c, resid, qy);
+                if (corr) s_my = fmax(s_my - F1 * qy, 0.0);
             }
         }
         __syncthreads();
         y = s_y;
-        zrep = (float)s_Z;
+        // Z relative to the target row's computed total; r_y / Z in one unit
+        zrep = (float)(s_Z / s_P);
         py = (float)(kind == KIND_RESID && resid ? s_my / s_Z : s_my);
     } else if (kind == KIND_GREEDY) {
-        y = st.y;
+        y = f.y;
     } else {
         kind = KIND_BAD;
-        a = 0;
         y = -1;
     }
+    const int a_out = kind == KIND_BAD ? 0 : a;
 
     for (int jj = tid; jj <= K; jj += kThreads) {
         int v = -1;
-        if (y >= 0) v = jj < a ? (jj == tid ? tok0 : p.tok[(long long)b * K + jj]) : (jj == a ? y : -1);
+        if (y >= 0) v = jj < a_out ? (jj == tid ? tok0 : p.tok[(long long)b * K + jj]) : (jj == a_out ? y : -1);
         p.out_tok[(long long)b * (K + 1) + jj] = v;
     }
+    // diagnostics of the rows the walk evaluated: lse of target rows 1..a+1,
+    // of the draft rows read (the tested positions, and with an open length
+    // walk every position up to L + 1), and the survivals
+    if (!GREEDY && kind != KIND_BAD) {
+        const int L = f.L;
+        const bool open = (w.seq[b].flags & SEQ_OPEN) != 0;
+        const int nd = OH ? 0 : (open ? min(L + 1, K) : min(a + 1, L));
+        for (int jj = tid; jj <= K; jj += kThreads) {
+            if (p.lse_t && jj <= a) p.lse_t[(long long)b * (K + 1) + jj] = (float)((double)w.row_m[rb + jj] * p.invT64 + log(w.row_s[rb + jj]));
+            if (p.lse_d && jj < nd) p.lse_d[(long long)b * K + jj] = (float)((double)w.row_m[rb + K + 1 + jj] * p.invT64 + log(w.row_s[rb + K + 1 + jj]));
+            if (p.surv && p.derived && !OH && open && jj < nd) p.surv[(long long)b * K + jj] = (float)w.srec[(long long)b * K + jj];
+        }
+        if (p.surv && p.derived && !OH && !open && tid == 0) {
+            // verify length fixed at plan time (tau <= 0): S_j over the draft rows read
+            double Sv = 1.0;
+            for (int jj = 0; jj < nd; ++jj) {
+                Sv = Sv / w.row_s[rb + K + 1 + jj];
+                p.surv[(long long)b * K + jj] = (float)Sv;
+            }
+        }
+    }
+    // rows and bytes streamed for this sequence (splits marked by sv_plan)
+    if (p.count) {
+        double rows = 0.0, elems = 0.0;
+        for (long long r = tid; r < R; r += kThreads) {
+            int any = 0;
+            for (int k = 0; k < p.nsplit; ++k)
+                if (__float_as_uint(w.part_m[(rb + r) * p.nsplit + k]) != kUnread) {
+                    any = 1;
+                    elems += (double)min(kSplit, p.V - k * kSplit);
+                }
+            rows += any;
+        }
+        rows = block_sum(rows, s_cnt);
+        elems = block_sum(elems, s_cnt);
+        if (tid == 0) {
+            if (p.rows_out) p.rows_out[b] = (int)rows;
+            if (p.bytes_out) p.bytes_out[b] = (long long)elems * (DT == SV_BF16 ? 2 : 4);
+        }
+    }
     if (tid == 0) {
-        p.acc_out[b] = a;
-        p.vl_out[b] = st.L;
+        p.acc_out[b] = a_out;
+        p.vl_out[b] = f.L;
         if (p.zmass) p.zmass[b] = zrep;
         if (p.pys) p.pys[b] = py;
-        if (p.rows_out) p.rows_out[b] = st.rows;
-        if (b == 0) {
-            // every kernel that can raise a status bit has finished; the word
-            // starts the next call at zero (it is zero from create on)
-            if (p.status_out) *p.status_out = w.ctl[CTL_STATUS];
-            w.ctl[CTL_STATUS] = 0;
+        int bits = 0;
+        if (kind == KIND_BAD) bits |= (f.L < 0 && !(w.seq[b].flags & SEQ_BAD)) ? SV_STATUS_INCOMPLETE : SV_STATUS_BAD_INPUT;
+        if (p.status_out) {
+            // every workgroup raises its bits, then counts itself done; the
+            // last one reads the call's word and clears it for the next call
+            if (bits) or_status(&w.ctl[CTL_STATUS], bits);
+            stores_done();
+            if (add_ag(&w.ctl[CTL_DONE], 1) == p.B - 1) {
+                *p.status_out = ld_ag(&w.ctl[CTL_STATUS]);
+                st_ag(&w.ctl[CTL_STATUS], 0);
+            }
         }
     }
 }
@@ -1738,9 +1975,44 @@ __global__ void sv_conf_status_kernel(ConfParams q, AuxWork w)
 
 // ---------------------------------------------------------------- host side
 
-
-const char* const kKernelNames[K_COUNT] = {"sv_plan", "sv_rows", "sv_decide", "sv_resid", "sv_draw"};
+const char* const kKernelNames[K_COUNT] = {"sv_plan", "sv_stream", "sv_resid", "sv_draw"};
 constexpr int kMaxSlots = 64; // timed launches per run
+
+size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int nsplit_of(int V) { return (V + kSplit - 1) / kSplit; }
+
+// Carves the verify step's workspace for up to B sequences of up to K drafted
+// positions over a vocabulary of ns splits out of base (NULL: sizes only).
+// Returns the bytes it needs.
+size_t carve_work(char* base, long long B, int K, int ns, Work* w)
+{
+    const long long R = 2LL * K + 1;
+    size_t off = 0;
+    auto take = [&](size_t bytes) -> char* {
+        const size_t o = off;
+        off = align_up(off + bytes);
+        return base ? base + o : nullptr;
+    };
+    w->ctl = (int*)take(CTL_WORDS * sizeof(int));
+    w->seq = (SeqCtl*)take((size_t)B * sizeof(SeqCtl));
+    w->rcnt = (int*)take((size_t)(B * R) * sizeof(int));
+    w->pcnt = (int*)take((size_t)(B * (K + 2)) * sizeof(int));
+    w->dec = (int*)take((size_t)(B * (K + 1)) * sizeof(int));
+    w->part_m = (float*)take((size_t)(B * R * ns) * sizeof(float));
+    w->part_s = (double*)take((size_t)(B * R * ns) * sizeof(double));
+    w->part_d = (float*)take((size_t)(B * R * ns) * sizeof(float));
+    w->part_i = (int*)take((size_t)(B * R * ns) * sizeof(int));
+    w->row_m = (float*)take((size_t)(B * R) * sizeof(float));
+    w->row_s = (double*)take((size_t)(B * R) * sizeof(double));
+    w->row_g = (int*)take((size_t)(B * R) * sizeof(int));
+    w->xlog = (float*)take((size_t)(B * R) * sizeof(float));
+    w->srec = (double*)take((size_t)(B * K) * sizeof(double));
+    w->seg = (double*)take((size_t)(B * ns * kSegStride) * sizeof(double));
+    w->segq = (double*)take((size_t)(B * ns * kSegStride) * sizeof(double));
+    w->kp = (double*)take((size_t)(B * ns * kParts * kKpStride) * sizeof(double));
+    return off;
+}
 
 } // namespace
 
@@ -1757,82 +2029,67 @@ struct spec_verify {
 
 namespace {
 
-// Launches one kernel of a step (256 threads per workgroup) on stream s.  While
-// per-kernel timing is on, the start and stop events are attached to the
-// dispatch itself (hipExtLaunchKernelGGL), so they time the kernel's execution
-// and not the queue around it.
+// Launches kernel on stream s with block threads per workgroup and returns the
+// launch's own status.  With start and stop events the events are attached to
+// the dispatch itself (hipExtLaunchKernel), so they time the kernel's
+// execution and not the queue around it.
+template <typename... KArgs, typename... Args>
+hipError_t launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, uint32_t shmem, hipStream_t s, hipEvent_t e0,
+                         hipEvent_t e1, Args... args)
+{
+    std::tuple<KArgs...> t(args...);
+    void* a[sizeof...(KArgs)];
+    std::apply([&](auto&... x) {
+        int i = 0;
+        ((a[i++] = (void*)&x), ...);
+    }, t);
+    if (e0) return hipExtLaunchKernel((const void*)kernel, grid, block, a, shmem, s, e0, e1, 0);
+    return hipLaunchKernel((const void*)kernel, grid, block, a, shmem, s);
+}
+
+// Launches the kernels of a step; while per-kernel timing is on, each launch
+// carries its own start and stop events.  Keeps the first failing status.
 struct StepLauncher {
     const spec_verify* h;
     hipStream_t s;
     bool timing;
     int slot;
+    hipError_t err;
     template <typename F, typename... Args>
     void operator()(int k, F kernel, dim3 grid, uint32_t shmem, Args... args)
     {
+        if (err != hipSuccess) return;
+        hipEvent_t e0 = nullptr, e1 = nullptr;
         if (timing && slot < kMaxSlots) {
             const int idx = h->timing_n * kMaxSlots + slot;
-            hipExtLaunchKernelGGL(kernel, grid, dim3(kThreads), shmem, s, h->ev[idx * 2], h->ev[idx * 2 + 1], 0,
-                                  args...);
+            e0 = h->ev[idx * 2];
+            e1 = h->ev[idx * 2 + 1];
             h->ev_kernel[idx] = k;
             ++slot;
-        } else {
-            hipLaunchKernelGGL(kernel, grid, dim3(kThreads), shmem, s, args...);
         }
+        err = launch_kernel(kernel, grid, dim3(kThreads), shmem, s, e0, e1, args...);
     }
 };
 
-// One verification step on stream s: plan, then per position group the row
-// statistics and the decisions (those of the last group inside the residual
-// pass when there is one), then the residual masses and the final draw.
-// Groups hold 3, 3, 4, 8, 16, 16, ... positions (a remainder of one position
-// joins the previous group).  Early groups are small because most sequences
-// stop early; each group costs a fixed few microseconds (the launches' ramp and
-// drain and the decisions), rows past a rejection inside a group are read for
-// nothing.  At B = 256, K = 16 with about 3.8 accepted positions per sequence
-// this schedule (3, 3, 4, 7) measured 4.5 us per step less than 2, 2, 4, 9.
+// One verification step on stream s: plan, the row statistics with in-launch
+// decisions (one launch per kChunkPos positions), the residual masses, and the
+// final draw.
 template <int DT, bool VEC, bool GR, int MODE, typename Launch>
-void enqueue_step(const spec_verify* h, const Params& p, hipStream_t s, Launch& launch)
+void enqueue_step(const Params& p, const Work& w, hipStream_t s, Launch& launch)
 {
     constexpr bool OH = (MODE & MODE_ONEHOT) != 0;
-    const unsigned B = (unsigned)p.B;
-    int gj[kMaxGroups], gn[kMaxGroups], ng = 0;
-    const int npos = p.K + 1;
-    static const int kFirst[] = {3, 3, 4, 8};
-    const int nfirst = (int)(sizeof(kFirst) / sizeof(kFirst[0]));
-    for (int j0 = 1; j0 <= npos; ++ng) {
-        int G = ng < nfirst ? kFirst[ng] : min(kFirst[nfirst - 1] << (ng - nfirst + 1), kMaxGroup);
-        if (npos - (j0 + G - 1) <= 1) G = npos - j0 + 1;
-        if (G > kMaxGroup) G = kMaxGroup;
-        gj[ng] = j0;
-        gn[ng] = G;
-        j0 += G;
+    constexpr unsigned SLOTS = (GR || OH) ? 1u : 2u;
+    const unsigned B = (unsigned)p.B, ns = (unsigned)p.nsplit;
+    const unsigned long long R = 2ull * p.K + 1;
+    launch(K_PLAN, sv_plan_kernel, dim3((unsigned)((B * R + kThreads - 1) / kThreads)), 0, p, w);
+    for (int j0 = 1; j0 <= p.K + 1; j0 += kChunkPos) {
+        const unsigned np = (unsigned)std::min(kChunkPos, p.K + 2 - j0);
+        launch(K_STREAM, sv_stream_kernel<DT, VEC, GR, MODE>, dim3(np * B * SLOTS * ns), 0, p, w, j0);
     }
-    auto slots = [&](int g) { return (GR || OH) ? gn[g] : 2 * gn[g]; };
-    launch(K_PLAN, sv_plan_kernel, dim3((B + kThreads - 1) / kThreads), 0, p, h->w);
-    // With a residual pass (sampling with draft probabilities) that pass takes
-    // the last group's decisions; otherwise each group has its own launch.
-    constexpr bool FUSED_LAST = !GR && !OH;
-    for (int g = 0; g < ng; ++g) {
-        const long long nrow = (long long)B * slots(g);
-        if (VEC && g >= 3 && g + 1 == ng) // (the unaligned path keeps one row per workgroup)
-            launch(K_ROWS, sv_rows_late_kernel<DT, true, GR, MODE>,
-                   dim3((unsigned)((nrow + kRowsLate - 1) / kRowsLate * p.nsplit)), 0, p, h->w, gj[g], gn[g]);
-        else
-            launch(K_ROWS, sv_rows_kernel<DT, VEC, GR, MODE>, dim3((unsigned)(nrow * p.nsplit)), 0, p, h->w, gj[g],
-                   gn[g]);
-        if (FUSED_LAST && g + 1 == ng) break;
-        launch(K_DECIDE, sv_decide_kernel<DT, GR, MODE & MODE_ONEHOT>, dim3(B), 0, p, h->w, gj[g], gn[g]);
-    }
-    if constexpr (FUSED_LAST) // (one-hot drafts: the final draw forms p without x itself)
-        launch(K_RESID, sv_resid_kernel<DT, VEC, MODE>, dim3(B * (unsigned)p.nsplit * kParts), 0, p, h->w, gj[ng - 1],
-               gn[ng - 1]);
-    launch(K_DRAW, sv_draw_kernel<DT, VEC, MODE>, dim3(B), (uint32_t)(p.nsplit * Seg<DT>::SEGS * sizeof(double)), p,
-           h->w, (const SeqState*)(FUSED_LAST ? h->w.fin : h->w.st));
+    if constexpr (!GR && !OH)
+        launch(K_RESID, sv_resid_kernel<DT, VEC, MODE>, dim3(B * ns * kParts), 0, p, w);
+    launch(K_DRAW, sv_draw_kernel<DT, VEC, GR, MODE>, dim3(B), (uint32_t)(ns * Seg<DT>::SEGS * sizeof(double)), p, w);
 }
-
-size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
-
-int nsplit_of(int V) { return (V + kSplit - 1) / kSplit; }
 
 bool args_vec_ok(const spec_verify_config* cfg, const spec_verify_args* a)
 {
@@ -1862,6 +2119,102 @@ struct DeviceGuard {
     }
 };
 
+int check_config(const spec_verify_config* cfg)
+{
+    if (!cfg) return SV_EINVAL;
+    if (cfg->max_batch < 1 || cfg->max_batch > SV_MAX_BATCH) return SV_EINVAL;
+    if (cfg->max_draft < 1 || cfg->max_draft > SV_MAX_DRAFT) return SV_EINVAL;
+    if (cfg->vocab < 1 || cfg->vocab > SV_MAX_VOCAB) return SV_EINVAL;
+    if (cfg->dtype != SV_F32 && cfg->dtype != SV_BF16) return SV_EUNSUPPORTED;
+    if (cfg->device < 0) return SV_EINVAL;
+    // A launch's work-item count must fit in 32 bits.  The largest launches:
+    // sv_stream over a chunk of positions (at most min(kChunkPos, K + 1), a
+    // target and a draft row each), sv_resid and sv_plan.
+    const long long ns = nsplit_of(cfg->vocab);
+    const long long gmax = std::min(kChunkPos, cfg->max_draft + 1);
+    const long long rows_wg = (long long)cfg->max_batch * 2 * gmax * ns;
+    const long long resid_wg = (long long)cfg->max_batch * ns * kParts;
+    if (std::max(rows_wg, resid_wg) * kThreads > 0xffffffffll) return SV_EUNSUPPORTED;
+    return SV_OK;
+}
+
+// Fills the kernels' parameters of one call (after spec_verify_check).
+Params make_params(const spec_verify_config* cfg, const spec_verify_args* a)
+{
+    const bool greedy = !(a->temperature > 0.0f);
+    Params p;
+    memset(&p, 0, sizeof(p));
+    p.B = a->B;
+    p.K = a->K;
+    p.V = cfg->vocab;
+    p.nsplit = nsplit_of(cfg->vocab);
+    p.greedy = greedy;
+    p.len_mode = a->length_mode;
+    p.derived = (a->length_mode == SV_LEN_TAU && !a->confidence) ? 1 : 0;
+    p.onehot = (!greedy && a->draft_mode == SV_DRAFT_ONEHOT) ? 1 : 0;
+    p.count = (a->rows_read || a->bytes_read) ? 1 : 0;
+    p.toff = (const long long*)a->target_row_offsets;
+    p.doff = (greedy || p.onehot) ? nullptr : (const long long*)a->draft_row_offsets;
+    p.t = a->target_logits;
+    p.tbs = a->target_batch_stride;
+    p.trs = a->target_row_stride;
+    p.d = a->draft_logits;
+    p.dbs = a->draft_batch_stride;
+    p.drs = a->draft_row_stride;
+    p.tok = a->draft_tokens;
+    p.u = a->uniforms;
+    p.vl_in = a->length_mode == SV_LEN_FIXED ? a->verify_len_in : nullptr;
+    p.conf = a->length_mode == SV_LEN_TAU ? a->confidence : nullptr;
+    p.tau = a->length_mode == SV_LEN_TAU ? a->tau : nullptr;
+    if (!greedy) {
+        p.invT64 = 1.0 / (double)a->temperature;
+        p.c64 = 1.4426950408889634073599246810019 / (double)a->temperature;
+        float hi = (float)p.c64;
+        if ((double)hi > p.c64) hi = nextafterf(hi, 0.0f);
+        float lo = (float)(p.c64 - (double)hi);
+        if (!(lo > 1e-37f)) lo = 1e-37f;
+        p.c_hi = hi;
+        p.c_lo = lo;
+        p.c32 = (float)p.c64;
+    }
+    p.acc_out = a->accepted_len;
+    p.out_tok = a->out_tokens;
+    p.vl_out = a->verify_len_out;
+    p.lse_t = a->lse_target;
+    p.lse_d = a->lse_draft;
+    p.surv = a->survival;
+    p.zmass = a->residual_mass;
+    p.pys = a->sampled_prob;
+    p.rows_out = a->rows_read;
+    p.bytes_out = (long long*)a->bytes_read;
+    p.status_out = a->device_status;
+    return p;
+}
+
+// Enqueues one checked call's kernels with workspace w.
+template <typename Launch>
+void enqueue_call(const spec_verify_config* cfg, const spec_verify_args* a, const Work& w, hipStream_t s,
+                  Launch& launch)
+{
+    const Params p = make_params(cfg, a);
+    const bool vec = args_vec_ok(cfg, a);
+    const int mode = (p.onehot ? MODE_ONEHOT : 0) | (p.toff ? MODE_PACKED : 0);
+    // runtime choices -> kernel variants (greedy steps never take the one-hot variant)
+#define SV_STEP(DT, VEC, GR, M) enqueue_step<DT, VEC, GR, M>(p, w, s, launch)
+#define SV_STEP_M(DT, VEC, GR) do { switch (GR ? (mode & MODE_PACKED) : mode) { \
+        case 0: SV_STEP(DT, VEC, GR, 0); break; case 1: SV_STEP(DT, VEC, GR, 1); break; \
+        case 2: SV_STEP(DT, VEC, GR, 2); break; default: SV_STEP(DT, VEC, GR, 3); break; } } while (0)
+    if (cfg->dtype == SV_BF16) {
+        if (vec) { if (p.greedy) SV_STEP_M(SV_BF16, true, true); else SV_STEP_M(SV_BF16, true, false); }
+        else { if (p.greedy) SV_STEP_M(SV_BF16, false, true); else SV_STEP_M(SV_BF16, false, false); }
+    } else {
+        if (vec) { if (p.greedy) SV_STEP_M(SV_F32, true, true); else SV_STEP_M(SV_F32, true, false); }
+        else { if (p.greedy) SV_STEP_M(SV_F32, false, true); else SV_STEP_M(SV_F32, false, false); }
+    }
+#undef SV_STEP_M
+#undef SV_STEP
+}
+
 } // namespace
 
 extern "C" {
@@ -1881,25 +2234,6 @@ const char* spec_verify_status_string(int status)
 int32_t spec_verify_kernel_count(void) { return K_COUNT; }
 
 const char* spec_verify_kernel_name(int32_t k) { return (k >= 0 && k < K_COUNT) ? kKernelNames[k] : ""; }
-
-static int check_config(const spec_verify_config* cfg)
-{
-    if (!cfg) return SV_EINVAL;
-    if (cfg->max_batch < 1 || cfg->max_batch > SV_MAX_BATCH) return SV_EINVAL;
-    if (cfg->max_draft < 1 || cfg->max_draft > SV_MAX_DRAFT) return SV_EINVAL;
-    if (cfg->vocab < 1 || cfg->vocab > SV_MAX_VOCAB) return SV_EINVAL;
-    if (cfg->dtype != SV_F32 && cfg->dtype != SV_BF16) return SV_EUNSUPPORTED;
-    if (cfg->device < 0) return SV_EINVAL;
-    // A launch's work-item count must fit in 32 bits.  The largest launches:
-    // sv_rows over the widest position group (at most min(kMaxGroup, K + 1)
-    // positions, a target and a draft row each) and sv_resid.
-    const long long ns = nsplit_of(cfg->vocab);
-    const long long gmax = std::min(kMaxGroup, cfg->max_draft + 1);
-    const long long rows_wg = (long long)cfg->max_batch * 2 * gmax * ns;
-    const long long resid_wg = (long long)cfg->max_batch * ns * kParts;
-    if (std::max(rows_wg, resid_wg) * kThreads > 0xffffffffll) return SV_EUNSUPPORTED;
-    return SV_OK;
-}
 
 int spec_verify_check(const spec_verify_config* cfg, const spec_verify_args* a)
 {
@@ -1950,19 +2284,8 @@ int spec_verify_create(const spec_verify_config* cfg, spec_verify_t** out)
     if (!h) return SV_ENOMEM;
     h->cfg = *cfg;
     h->nsplit = nsplit_of(cfg->vocab);
-    const long long nrow = (long long)cfg->max_batch * (2 * cfg->max_draft + 1);
-    const size_t ns = (size_t)h->nsplit;
-    size_t off = 0;
-    const size_t o_ctl = off; off = align_up(off + CTL_WORDS * sizeof(int));
-    const size_t o_pm = off; off = align_up(off + nrow * ns * sizeof(float));
-    const size_t o_ps = off; off = align_up(off + nrow * ns * sizeof(double));
-    const size_t o_pi = off; off = align_up(off + nrow * ns * sizeof(int));
-    const size_t o_pd = off; off = align_up(off + nrow * ns * sizeof(float));
-    const size_t o_st = off; off = align_up(off + (size_t)cfg->max_batch * sizeof(SeqState));
-    const size_t o_fi = off; off = align_up(off + (size_t)cfg->max_batch * sizeof(SeqState));
-    const size_t o_lv = off; off = align_up(off + (size_t)cfg->max_batch * sizeof(int));
-    const size_t o_sg = off; off = align_up(off + (size_t)cfg->max_batch * ns * kSegStride * sizeof(double));
-    const size_t o_xl = off; off = align_up(off + nrow * sizeof(float));
+    const size_t verify_bytes = carve_work(nullptr, cfg->max_batch, cfg->max_draft, h->nsplit, &h->w);
+    size_t off = align_up(verify_bytes);
     const long long ncand = std::min((long long)cfg->max_batch * cfg->max_draft, (long long)SV_MAX_SCHED_CANDIDATES);
     const size_t o_ss = off; off = align_up(off + (size_t)ncand * sizeof(double));
     const size_t o_sr = off; off = align_up(off + (size_t)ncand * sizeof(int));
@@ -1973,16 +2296,7 @@ int spec_verify_create(const spec_verify_config* cfg, spec_verify_t** out)
     const size_t o_cc = off; off = align_up(off + (conf_ok ? (size_t)cfg->max_batch * sizeof(int) : 0));
     if (hipMalloc(&h->ws, off) != hipSuccess) { free(h); return SV_ENOMEM; }
     char* base = (char*)h->ws;
-    h->w.ctl = (int*)(base + o_ctl);
-    h->w.part_m = (float*)(base + o_pm);
-    h->w.part_s = (double*)(base + o_ps);
-    h->w.part_d = (float*)(base + o_pd);
-    h->w.part_i = (int*)(base + o_pi);
-    h->w.st = (SeqState*)(base + o_st);
-    h->w.fin = (SeqState*)(base + o_fi);
-    h->w.live = (int*)(base + o_lv);
-    h->w.seg = (double*)(base + o_sg);
-    h->w.xlog = (float*)(base + o_xl);
+    carve_work(base, cfg->max_batch, cfg->max_draft, h->nsplit, &h->w);
     h->aux.ctl = h->w.ctl;
     h->aux.sched_s = (double*)(base + o_ss);
     h->aux.sched_rank = (int*)(base + o_sr);
@@ -1991,8 +2305,8 @@ int spec_verify_create(const spec_verify_config* cfg, spec_verify_t** out)
     h->aux.conf_head = conf_ok ? (int*)(base + o_ch) : nullptr;
     h->aux.conf_count = conf_ok ? (int*)(base + o_cc) : nullptr;
     h->aux.conf_K = cfg->max_draft;
-    // control words (status bits) start at zero; each call clears what it reports;
-    // the confidence history starts empty
+    // control words (status bits of the admission and confidence calls) start at
+    // zero; each call clears what it reports; the confidence history starts empty
     bool zero_ok = hipMemset(h->w.ctl, 0, CTL_WORDS * sizeof(int)) == hipSuccess;
     if (conf_ok) {
         zero_ok = zero_ok && hipMemset(base + o_cr, 0, o_cc + (size_t)cfg->max_batch * sizeof(int) - o_cr) == hipSuccess;
@@ -2109,9 +2423,9 @@ int spec_verify_confidence(spec_verify_t* h, const spec_verify_conf_args* a, voi
     q.now_out = a->conf_now;
     q.out = a->conf_out;
     q.status_out = a->device_status;
-    hipLaunchKernelGGL(sv_conf_kernel, dim3(a->B), dim3(kThreads), 0, s, q, h->aux);
-    hipLaunchKernelGGL(sv_conf_status_kernel, dim3(1), dim3(64), 0, s, q, h->aux);
-    return hipGetLastError() == hipSuccess ? SV_OK : SV_EDEVICE;
+    hipError_t e = launch_kernel(sv_conf_kernel, dim3(a->B), dim3(kThreads), 0, s, nullptr, nullptr, q, h->aux);
+    if (e == hipSuccess) e = launch_kernel(sv_conf_status_kernel, dim3(1), dim3(64), 0, s, nullptr, nullptr, q, h->aux);
+    return e == hipSuccess ? SV_OK : SV_EDEVICE;
 }
 
 int spec_verify_sched_check(const spec_verify_config* cfg, const spec_verify_sched_args* a)
@@ -2148,10 +2462,12 @@ int spec_verify_schedule(spec_verify_t* h, const spec_verify_sched_args* a, void
     q.expected = a->expected_rate;
     q.status_out = a->device_status;
     const unsigned N = (unsigned)(a->B * a->K);
-    hipLaunchKernelGGL(sv_sched_surv_kernel, dim3((a->B + kThreads - 1) / kThreads), dim3(kThreads), 0, s, q, h->aux);
-    hipLaunchKernelGGL(sv_sched_rank_kernel, dim3(N), dim3(kThreads), 0, s, q, h->aux);
-    hipLaunchKernelGGL(sv_sched_pick_kernel, dim3(1), dim3(kSchedThreads), 0, s, q, h->aux);
-    return hipGetLastError() == hipSuccess ? SV_OK : SV_EDEVICE;
+    hipError_t e = launch_kernel(sv_sched_surv_kernel, dim3((a->B + kThreads - 1) / kThreads), dim3(kThreads), 0, s,
+                                 nullptr, nullptr, q, h->aux);
+    if (e == hipSuccess) e = launch_kernel(sv_sched_rank_kernel, dim3(N), dim3(kThreads), 0, s, nullptr, nullptr, q, h->aux);
+    if (e == hipSuccess)
+        e = launch_kernel(sv_sched_pick_kernel, dim3(1), dim3(kSchedThreads), 0, s, nullptr, nullptr, q, h->aux);
+    return e == hipSuccess ? SV_OK : SV_EDEVICE;
 }
 
 int spec_verify_run(spec_verify_t* h, const spec_verify_args* a, void* hip_stream)
@@ -2161,78 +2477,11 @@ int spec_verify_run(spec_verify_t* h, const spec_verify_args* a, void* hip_strea
     if (rc != SV_OK) return rc;
     if (a->B == 0) return SV_OK;
     DeviceGuard guard(h->cfg.device);
-    hipStream_t s = (hipStream_t)hip_stream;
-
-    const bool greedy = !(a->temperature > 0.0f);
-    const bool vec = args_vec_ok(&h->cfg, a);
-    Params p;
-    memset(&p, 0, sizeof(p));
-    p.B = a->B;
-    p.K = a->K;
-    p.V = h->cfg.vocab;
-    p.nsplit = h->nsplit;
-    p.seg_w = 1;
-    while (p.seg_w < p.nsplit) p.seg_w <<= 1;
-    p.greedy = greedy;
-    p.len_mode = a->length_mode;
-    p.derived = (a->length_mode == SV_LEN_TAU && !a->confidence) ? 1 : 0;
-    p.onehot = (!greedy && a->draft_mode == SV_DRAFT_ONEHOT) ? 1 : 0;
-    p.toff = (const long long*)a->target_row_offsets;
-    p.doff = (greedy || p.onehot) ? nullptr : (const long long*)a->draft_row_offsets;
-    p.t = a->target_logits;
-    p.tbs = a->target_batch_stride;
-    p.trs = a->target_row_stride;
-    p.d = a->draft_logits;
-    p.dbs = a->draft_batch_stride;
-    p.drs = a->draft_row_stride;
-    p.tok = a->draft_tokens;
-    p.u = a->uniforms;
-    p.vl_in = a->length_mode == SV_LEN_FIXED ? a->verify_len_in : nullptr;
-    p.conf = a->length_mode == SV_LEN_TAU ? a->confidence : nullptr;
-    p.tau = a->length_mode == SV_LEN_TAU ? a->tau : nullptr;
-    if (!greedy) {
-        p.invT64 = 1.0 / (double)a->temperature;
-        p.c64 = 1.4426950408889634073599246810019 / (double)a->temperature;
-        float hi = (float)p.c64;
-        if ((double)hi > p.c64) hi = nextafterf(hi, 0.0f);
-        float lo = (float)(p.c64 - (double)hi);
-        if (!(lo > 1e-37f)) lo = 1e-37f;
-        p.c_hi = hi;
-        p.c_lo = lo;
-        p.c32 = (float)p.c64;
-    }
-    p.acc_out = a->accepted_len;
-    p.out_tok = a->out_tokens;
-    p.vl_out = a->verify_len_out;
-    p.lse_t = a->lse_target;
-    p.lse_d = a->lse_draft;
-    p.surv = a->survival;
-    p.zmass = a->residual_mass;
-    p.pys = a->sampled_prob;
-    p.rows_out = a->rows_read;
-    p.status_out = a->device_status;
-
     const bool timing = h->ev && h->timing_n < h->timing_max;
-    StepLauncher launch{h, s, timing, 0};
-    const int bf = h->cfg.dtype == SV_BF16;
-    const int mode = (p.onehot ? MODE_ONEHOT : 0) | (p.toff ? MODE_PACKED : 0);
-    // runtime choices -> kernel variants (greedy steps never take the one-hot variant)
-#define SV_STEP(DT, VEC, GR, M) enqueue_step<DT, VEC, GR, M>(h, p, s, launch)
-#define SV_STEP_M(DT, VEC, GR) do { switch (GR ? (mode & MODE_PACKED) : mode) { \
-        case 0: SV_STEP(DT, VEC, GR, 0); break; case 1: SV_STEP(DT, VEC, GR, 1); break; \
-        case 2: SV_STEP(DT, VEC, GR, 2); break; default: SV_STEP(DT, VEC, GR, 3); break; } } while (0)
-    if (bf) {
-        if (vec) { if (greedy) SV_STEP_M(SV_BF16, true, true); else SV_STEP_M(SV_BF16, true, false); }
-        else { if (greedy) SV_STEP_M(SV_BF16, false, true); else SV_STEP_M(SV_BF16, false, false); }
-    } else {
-        if (vec) { if (greedy) SV_STEP_M(SV_F32, true, true); else SV_STEP_M(SV_F32, true, false); }
-        else { if (greedy) SV_STEP_M(SV_F32, false, true); else SV_STEP_M(SV_F32, false, false); }
-    }
-#undef SV_STEP_M
-#undef SV_STEP
+    StepLauncher launch{h, (hipStream_t)hip_stream, timing, 0, hipSuccess};
+    enqueue_call(&h->cfg, a, h->w, (hipStream_t)hip_stream, launch);
     if (timing) h->timing_n++;
-
-    return hipGetLastError() == hipSuccess ? SV_OK : SV_EDEVICE;
+    return launch.err == hipSuccess ? SV_OK : SV_EDEVICE;
 }
 
 } // extern "C"

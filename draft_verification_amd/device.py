@@ -51,6 +51,7 @@ class DeviceProblem:
     residual_mass: Optional[torch.Tensor] = None
     sampled_prob: Optional[torch.Tensor] = None
     rows_read: Optional[torch.Tensor] = None
+    bytes_read: Optional[torch.Tensor] = None
     device_status: Optional[torch.Tensor] = None
     draft_mode: int = B.SV_DRAFT_PROBS
     target_row_offsets: Optional[torch.Tensor] = None  # packed rows: [B+1] int64
@@ -87,6 +88,7 @@ class DeviceProblem:
         self.verify_len_out = torch.full((Bn,), -7, **i32)
         self.device_status = torch.full((1,), -7, **i32)
         self.rows_read = torch.full((Bn,), -7, **i32)
+        self.bytes_read = torch.full((Bn,), -7, dtype=torch.int64, device=device)
         if diagnostics:
             nan = float("nan")
             self.lse_target = torch.full((Bn, K + 1), nan, **f32)
@@ -104,12 +106,14 @@ class DeviceProblem:
             lse_target=self.lse_target, lse_draft=self.lse_draft, survival=self.survival,
             residual_mass=self.residual_mass, sampled_prob=self.sampled_prob, rows_read=self.rows_read,
             device_status=self.device_status, draft_mode=self.draft_mode,
-            target_row_offsets=self.target_row_offsets, draft_row_offsets=self.draft_row_offsets)
+            target_row_offsets=self.target_row_offsets, draft_row_offsets=self.draft_row_offsets,
+            bytes_read=self.bytes_read)
 
     def fetch(self) -> dict:
         torch.cuda.synchronize()
         out = {}
-        for name in ("accepted_len", "out_tokens", "verify_len_out", "device_status", "rows_read", "lse_target",
+        for name in ("accepted_len", "out_tokens", "verify_len_out", "device_status", "rows_read", "bytes_read",
+                     "lse_target",
                      "lse_draft", "survival", "residual_mass", "sampled_prob"):
             t = getattr(self, name)
             out[name] = None if t is None else t.cpu().numpy()

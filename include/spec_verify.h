@@ -62,9 +62,12 @@
  *                                 1 for a bonus draw; 0 if a rejection met Z <= 0
  *                                 (then the draw falls back to p); NaN for greedy
  *   sampled_prob   float [B]      probability of the final token under its draw
- *   rows_read      int32 [B]      logit rows (target + draft) streamed for the
- *                                 sequence; positions are walked in groups, so
- *                                 rows after a rejection inside its group count
+ *   rows_read      int32 [B]      logit rows (target + draft) of which the step
+ *                                 streamed at least one split for the sequence;
+ *                                 rows of positions dispatched before an earlier
+ *                                 rejection was known count
+ *   bytes_read     int64 [B]      logit bytes streamed for the sequence (each
+ *                                 streamed split of a row once)
  *   device_status  int32 [1]      0, or SV_STATUS_* bits (see below)
  *
  * Ownership: the caller owns every buffer and keeps it alive until the work
@@ -100,11 +103,14 @@ enum { SV_OK = 0, SV_EINVAL = -1, SV_ENOMEM = -2, SV_EDEVICE = -3, SV_EUNSUPPORT
 enum { SV_F32 = 0, SV_BF16 = 1 };
 enum { SV_LEN_FIXED = 0, SV_LEN_TAU = 1 };
 enum { SV_DRAFT_PROBS = 0, SV_DRAFT_ONEHOT = 1 };
-enum { SV_STATUS_BAD_INPUT = 1, SV_STATUS_TIMEOUT = 2 };
+/* device_status bits.  SV_STATUS_INCOMPLETE: a sequence's verify-length walk
+ * did not finish on the device (an internal consistency check; the sequence is
+ * reported like a bad one).  No valid input raises it. */
+enum { SV_STATUS_BAD_INPUT = 1, SV_STATUS_INCOMPLETE = 2 };
 
 /* Limits checked by spec_verify_create.  Besides these, the largest launch of
  * a configuration must stay within 2^32 - 1 work-items: max_batch *
- * 2 * min(16, max_draft + 1) * ceil(vocab / 16384) workgroups of 256 (and
+ * 2 * min(32, max_draft + 1) * ceil(vocab / 16384) workgroups of 256 (and
  * max_batch * ceil(vocab / 16384) * 2 of them); larger configurations return
  * SV_EUNSUPPORTED. */
 #define SV_MAX_VOCAB 1048576
@@ -160,6 +166,7 @@ typedef struct {
     const int64_t* draft_row_offsets;  /* packed draft rows, [B+1] likewise (L_b rows per sequence;
                                       a different count marks the sequence bad).  Required with
                                       target_row_offsets when T > 0 and SV_DRAFT_PROBS. */
+    int64_t* bytes_read;           /* optional [B] */
 } spec_verify_args;
 
 /* Allocate a handle and its workspace on cfg->device.  *out is set only on SV_OK. */

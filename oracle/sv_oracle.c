@@ -67,13 +67,10 @@ enum { SVO_MARGIN_ACCEPT = 1, SVO_MARGIN_CDF = 2, SVO_MARGIN_SURVIVAL = 4 };
  * confidence max_v q_j(v) is 1, and lse of the draft rows is not reported. */
 enum { SVO_DRAFT_PROBS = 0, SVO_DRAFT_ONEHOT = 1 };
 
+/* Margin of the bit-exact comparison: |u - p/q| at a tested position, and the
+ * final draw's CDF gap (distance of w to the nearest step of the running sum)
+ * relative to the draw's total mass Z (1 for a bonus draw). */
 #define SVO_MARGIN 1e-6
-/* The final draw's CDF gap (distance of w to the nearest step) is measured
- * relative to max(Z, SVO_Z_FLOOR).  Z = sum max(0, p - q) is a difference of
- * two unit masses: arithmetic on the token masses bounds its absolute error, so
- * a gap relative to Z alone is ill-conditioned as Z -> 0 (draft rows nearly
- * equal to the target rows).  A bonus draw has Z = 1. */
-#define SVO_Z_FLOOR 0.1
 
 typedef struct {
     int32_t B, K, V;
@@ -327,7 +324,7 @@ static void verify_one(const svo_problem* P, int32_t b, int32_t i, const svo_res
                 }
                 kind = SVO_FINAL_RESIDUAL;
                 if (Zr > 0.0) {
-                    y = inverse_cdf(r, V, uf * Zr, fmax(Zr, SVO_Z_FLOOR), &cdf_gap, &alt);
+                    y = inverse_cdf(r, V, uf * Zr, Zr, &cdf_gap, &alt);
                     Z = Zr;
                     py = r[y] / Zr;
                 } else {

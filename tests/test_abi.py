@@ -44,7 +44,7 @@ def test_status_strings_and_kernel_names(B):
     assert "invalid" in B.status_string(B.SV_EINVAL)
     assert B.status_string(12345) == "unknown status"
     names = B.kernel_names()
-    assert names == ["sv_plan", "sv_rows", "sv_decide", "sv_resid", "sv_draw"]
+    assert names == ["sv_plan", "sv_stream", "sv_resid", "sv_draw"]
     assert B.lib().spec_verify_kernel_name(99) == b""
 
 
@@ -108,7 +108,8 @@ def test_bad_configs_are_rejected_before_device_work(B, cfg):
 
 
 def test_launches_beyond_32_bit_work_item_counts_are_rejected(B):
-    # 1048575 sequences x 16-position groups x 8 splits: 2^28 workgroups of 256
+    # 1048575 sequences x 17 positions x 2 rows x 8 splits in one launch of the
+    # row statistics: far more than 2^32 work-items
     c = B.Config(1048575, 16, 129280, B.SV_BF16, 0)
     assert B.check(c, B.Args()) == B.SV_EUNSUPPORTED
     h = ctypes.c_void_p()
@@ -118,9 +119,10 @@ def test_launches_beyond_32_bit_work_item_counts_are_rejected(B):
     # configuration passes; the empty arguments are what is rejected)
     c = B.Config(1048575, 1, 8, B.SV_F32, 0)
     assert B.check(c, B.Args()) == B.SV_EINVAL
-    # at V = 129280 and K = 16 the bound allows 65535 sequences, not 65536
-    assert B.check(B.Config(65535, 16, 129280, B.SV_BF16, 0), B.Args()) == B.SV_EINVAL
-    assert B.check(B.Config(65536, 16, 129280, B.SV_BF16, 0), B.Args()) == B.SV_EUNSUPPORTED
+    # at V = 129280 and K = 16 one launch covers 17 positions x 2 rows x 8
+    # splits per sequence: (2^32 - 1) // (256 * 272) = 61680 sequences fit
+    assert B.check(B.Config(61680, 16, 129280, B.SV_BF16, 0), B.Args()) == B.SV_EINVAL
+    assert B.check(B.Config(61681, 16, 129280, B.SV_BF16, 0), B.Args()) == B.SV_EUNSUPPORTED
 
 
 def test_destroy_null_is_a_no_op(B):

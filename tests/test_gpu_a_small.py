@@ -32,7 +32,7 @@ def _run_case(name, w, *, prob=None, derived=False, seqs=None, sv=None):
     dp = D.from_problem(prob)
     res = D.run_once(dp, sv)
     orc = O.verify_problem(prob, seqs=seqs, all_rows=True)
-    rep = PU.compare(name, res, orc, dtype=w.dtype, greedy=w.temperature == 0, derived=derived)
+    rep = PU.compare(name, res, orc, dtype=w.dtype, greedy=w.temperature == 0, prob=prob)
     print(rep.line(), flush=True)
     assert not rep.mismatches, rep.mismatches[:5]
     return res, orc, rep

@@ -154,6 +154,6 @@ def test_schedule_feeds_a_verify_step():
     np.testing.assert_array_equal(vl.cpu().numpy(), o_s.verify_len)
     prob.verify_len = o_s.verify_len.astype(np.int32)
     orc = O.verify_problem(prob, all_rows=True)
-    rep = PU.compare("schedule -> verify", res, orc, dtype=w.dtype, greedy=False, derived=False)
+    rep = PU.compare("schedule -> verify", res, orc, dtype=w.dtype, greedy=False, prob=prob)
     print(rep.line(), flush=True)
     assert not rep.mismatches, rep.mismatches[:5]

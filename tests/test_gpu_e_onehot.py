@@ -25,7 +25,7 @@ def _run(name, w, prob=None, derived=False):
     dp = D.from_problem(prob)
     res = D.run_once(dp)
     orc = O.verify_problem(prob, all_rows=True)
-    rep = PU.compare(name, res, orc, dtype=w.dtype, derived=derived)
+    rep = PU.compare(name, res, orc, dtype=w.dtype, prob=prob)
     print(rep.line(), flush=True)
     assert not rep.mismatches, rep.mismatches[:5]
     assert np.isnan(res["lse_draft"]).all()          # not written in one-hot mode

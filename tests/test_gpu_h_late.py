@@ -30,7 +30,7 @@ def _run(name, w, *, prob=None, derived=False, packed=False):
         dp = D.from_problem(prob)
     res = D.run_once(dp)
     orc = O.verify_problem(prob, all_rows=True)
-    rep = PU.compare(name, res, orc, dtype=w.dtype, greedy=w.temperature == 0, derived=derived)
+    rep = PU.compare(name, res, orc, dtype=w.dtype, greedy=w.temperature == 0, prob=prob)
     print(rep.line(), flush=True)
     assert not rep.mismatches, rep.mismatches[:5]
     return res, orc

@@ -1,7 +1,7 @@
 """GPU parity at the library's size limits: the largest vocabulary
-(SV_MAX_VOCAB = 2^20 tokens: 64 splits, so a group's partials span more than one
-workgroup's threads in sv_decide), the longest draft block (SV_MAX_DRAFT = 256:
-about twenty position groups) and the largest batch (SV_MAX_BATCH sequences).
+(SV_MAX_VOCAB = 2^20 tokens: 64 splits, so a row's merge takes every lane of a
+wavefront), the longest draft block (SV_MAX_DRAFT = 256: nine launches of the
+row statistics) and the largest batch (SV_MAX_BATCH sequences).
 Each case is compared with the CPU oracle (tests/parity_util.py states the
 bar; the largest batch compares the decisions array-wise)."""
 import numpy as np
@@ -25,7 +25,7 @@ def _run(name, w, *, derived=False):
     prob = synth.make_problem(w)
     res = D.run_once(D.from_problem(prob))
     orc = O.verify_problem(prob, all_rows=True)
-    rep = PU.compare(name, res, orc, dtype=w.dtype, greedy=w.temperature == 0, derived=derived)
+    rep = PU.compare(name, res, orc, dtype=w.dtype, greedy=w.temperature == 0, prob=prob)
     print(rep.line(), flush=True)
     assert not rep.mismatches, rep.mismatches[:5]
     return res, orc

@@ -61,7 +61,7 @@ def test_strided_logits(dtype, pad, gap, shift, T):
         dp.draft, dp.draft_strides = d, (dbs, drs)
     res = D.run_once(dp)
     orc = O.verify_problem(prob, all_rows=True)
-    rep = PU.compare(f"strides {dtype} {pad} {gap} {shift} {T}", res, orc, dtype=dtype, greedy=T == 0.0)
+    rep = PU.compare(f"strides {dtype} {pad} {gap} {shift} {T}", res, orc, dtype=dtype, greedy=T == 0.0, prob=prob)
     print(rep.line(), flush=True)
     assert not rep.mismatches, rep.mismatches[:5]
     assert res["device_status"][0] == 0

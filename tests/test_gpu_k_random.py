@@ -61,7 +61,6 @@ def test_random_workload(i):
         dp = D.from_problem(prob)
     res = D.run_once(dp)
     orc = O.verify_problem(prob, all_rows=True)
-    rep = PU.compare(f"random {i}", res, orc, dtype=w.dtype, greedy=w.temperature == 0,
-                     derived=(mode == "tau_derived"))
+    rep = PU.compare(f"random {i}", res, orc, dtype=w.dtype, greedy=w.temperature == 0, prob=prob)
     print(rep.line(), flush=True)
     assert not rep.mismatches, rep.mismatches[:5]

@@ -411,11 +411,11 @@ def test_accept_margin_is_flagged():
     assert r.margin[0] & O.MARGIN_ACCEPT
 
 
-@pytest.mark.parametrize("noise", [0.01, 1.0])
-def test_cdf_gap_is_relative_to_residual_mass_with_a_floor(noise):
+@pytest.mark.parametrize("noise", [0.002, 0.01, 1.0])
+def test_cdf_gap_is_relative_to_residual_mass(noise):
     # The final draw's CDF gap (distance of w = u Z to the nearest step of
-    # cumsum(max(0, p - q))) is reported relative to max(Z, 0.1); nearly equal
-    # rows (noise 0.01) give Z well below 0.1, unequal rows (noise 1) above it.
+    # cumsum(max(0, p - q))) is reported relative to Z itself; nearly equal
+    # rows (noise 0.002, 0.01) give Z far below 1, unequal rows (noise 1) not.
     rng = _rng(17)
     B, K, V = 60, 1, 300
     t, d, _, u = _problem(rng, B, K, V, noise=noise)
@@ -437,8 +437,9 @@ def test_cdf_gap_is_relative_to_residual_mass_with_a_floor(noise):
         w = np.float64(u[b, K]) * Z
         y = int(np.searchsorted(C, w, side="right"))
         gap = min(abs(w - (C[y - 1] if y > 0 else 0.0)), abs(C[y] - w))
-        np.testing.assert_allclose(r.cdf_gap[b], gap / max(Z, 0.1), rtol=1e-6, atol=1e-15)
-        assert bool(r.margin[b] & O.MARGIN_CDF) == (gap / max(Z, 0.1) < 1e-6)
+        np.testing.assert_allclose(r.residual_mass[b], Z, rtol=1e-10)
+        np.testing.assert_allclose(r.cdf_gap[b], gap / Z, rtol=1e-6, atol=1e-15)
+        assert bool(r.margin[b] & O.MARGIN_CDF) == (gap / Z < 1e-6)
         zs.append(Z)
     zs = np.array(zs)
-    assert (zs < 0.1).all() if noise < 0.1 else (zs > 0.1).all()
+    assert (zs < 0.05).all() if noise < 0.1 else (zs > 0.1).all()
