@@ -24,10 +24,11 @@ EXPORTED = (
     "spec_verify_create", "spec_verify_check", "spec_verify_run", "spec_verify_destroy",
     "spec_verify_status_string", "spec_verify_timing_begin", "spec_verify_timing_end",
     "spec_verify_kernel_count", "spec_verify_kernel_name", "spec_verify_sched_check", "spec_verify_schedule",
-    "spec_verify_conf_check", "spec_verify_confidence",
+    "spec_verify_conf_check", "spec_verify_confidence", "spec_verify_run_noalloc",
 )
 SV_MAX_CONF_DELAY = 4
 SV_MAX_SCHED_BATCH, SV_MAX_SCHED_CANDIDATES = 4096, 65536
+SV_NOALLOC_SCRATCH_BYTES = 16777216
 
 
 class Config(ctypes.Structure):
@@ -115,6 +116,8 @@ def lib() -> ctypes.CDLL:
         L.spec_verify_conf_check.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(ConfArgs)]
         L.spec_verify_confidence.restype = ctypes.c_int
         L.spec_verify_confidence.argtypes = [ctypes.c_void_p, ctypes.POINTER(ConfArgs), ctypes.c_void_p]
+        L.spec_verify_run_noalloc.restype = ctypes.c_int
+        L.spec_verify_run_noalloc.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(Args), ctypes.c_void_p]
         _lib = L
     return _lib
 
@@ -183,6 +186,17 @@ def conf_check(cfg: Config, args: ConfArgs) -> int:
 def sched_check(cfg: Config, args: SchedArgs) -> int:
     """Host-only check of an admission call (no device work)."""
     return int(lib().spec_verify_sched_check(ctypes.byref(cfg), ctypes.byref(args)))
+
+
+def run_noalloc(cfg: Config, args: Args, stream: Optional[int] = None) -> None:
+    """Enqueue one step without a handle: the library's static per-device
+    workspace, no device allocation (see spec_verify_run_noalloc)."""
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream(cfg.device).cuda_stream
+    rc = lib().spec_verify_run_noalloc(ctypes.byref(cfg), ctypes.byref(args), ctypes.c_void_p(stream))
+    if rc != SV_OK:
+        raise SpecVerifyError(rc, "spec_verify_run_noalloc")
 
 
 class SpecVerify:

@@ -70,6 +70,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <tuple>
 
 #include "spec_verify.h"
@@ -2016,6 +2017,13 @@ size_t carve_work(char* base, long long B, int K, int ns, Work* w)
 
 } // namespace
 
+// Workspace of spec_verify_run_noalloc: one copy per device, loaded with the
+// code object and held until the process ends.  Host code never passes this
+// name to a kernel or a copy (on the host it is only a stand-in for the
+// symbol): it uses the device address hipGetSymbolAddress returns for the
+// current device.
+static __device__ __align__(256) unsigned char scratch[SV_NOALLOC_SCRATCH_BYTES];
+
 struct spec_verify {
     spec_verify_config cfg;
     int nsplit;
@@ -2213,6 +2221,25 @@ void enqueue_call(const spec_verify_config* cfg, const spec_verify_args* a, cons
     }
 #undef SV_STEP_M
 #undef SV_STEP
+}
+
+// Device address of the scratch array on device dev (the current device),
+// looked up on the first call for that device and kept.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+int scratch_address(int dev, void** out)
+{
+    if (dev < 0 || dev >= kMaxDevices) return SV_EUNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return SV_EDEVICE;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return SV_OK;
 }
 
 } // namespace
@@ -2481,6 +2508,29 @@ int spec_verify_run(spec_verify_t* h, const spec_verify_args* a, void* hip_strea
     StepLauncher launch{h, (hipStream_t)hip_stream, timing, 0, hipSuccess};
     enqueue_call(&h->cfg, a, h->w, (hipStream_t)hip_stream, launch);
     if (timing) h->timing_n++;
+    return launch.err == hipSuccess ? SV_OK : SV_EDEVICE;
+}
+
+int spec_verify_run_noalloc(const spec_verify_config* cfg, const spec_verify_args* a, void* hip_stream)
+{
+    int rc = spec_verify_check(cfg, a);
+    if (rc != SV_OK) return rc;
+    if (a->B == 0) return SV_OK;
+    // the workspace of this call's B, K and vocabulary, carved from the array
+    const int ns = nsplit_of(cfg->vocab);
+    Work w;
+    if (carve_work(nullptr, a->B, a->K, ns, &w) > (size_t)SV_NOALLOC_SCRATCH_BYTES) return SV_EUNSUPPORTED;
+    int ndev = 0;
+    if (hipGetDeviceCount(&ndev) != hipSuccess || cfg->device >= ndev) return SV_EDEVICE;
+    DeviceGuard guard(cfg->device);
+    void* base = nullptr;
+    rc = scratch_address(cfg->device, &base);
+    if (rc != SV_OK) return rc;
+    carve_work((char*)base, a->B, a->K, ns, &w);
+    // sv_plan clears the counters and status words the step needs at zero
+    // (a kernel, not a memset); nothing else is read before it is written
+    StepLauncher launch{nullptr, (hipStream_t)hip_stream, false, 0, hipSuccess};
+    enqueue_call(cfg, a, w, (hipStream_t)hip_stream, launch);
     return launch.err == hipSuccess ? SV_OK : SV_EDEVICE;
 }
 

@@ -182,6 +182,28 @@ int spec_verify_check(const spec_verify_config* cfg, const spec_verify_args* a);
  * reads the pointers and sizes of the args it was captured with. */
 int spec_verify_run(spec_verify_t* h, const spec_verify_args* a, void* hip_stream);
 
+/* For callers that cannot allocate device memory at all (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): one
+ * verification step without a handle, identical in its outputs to
+ * spec_verify_run.  Its workspace is a static device array of
+ * SV_NOALLOC_SCRATCH_BYTES on cfg->device, loaded with the library and held
+ * until the process ends; the call allocates nothing (no hipMalloc, hipFree or
+ * allocating library routine) and only launches kernels on hip_stream.
+ *
+ * cfg gives the vocabulary, dtype and device, and the limits a->B and a->K are
+ * checked against (as for spec_verify_check).  The workspace the call needs
+ * grows with a->B, a->K and vocab: about 15 KB per sequence at K = 16 and
+ * V = 129280, so up to 1024 such sequences fit.  A call that needs more than
+ * the array returns SV_EUNSUPPORTED before any device work; other errors as
+ * for spec_verify_run (devices numbered 64 and above: SV_EUNSUPPORTED).
+ *
+ * The array is shared by every call on one device and keeps the last call's
+ * contents; each call's first kernel clears what must start at zero.  Calls
+ * that overlap on one device (other streams, other threads) race and give
+ * undefined results: serialise them. */
+#define SV_NOALLOC_SCRATCH_BYTES 16777216
+int spec_verify_run_noalloc(const spec_verify_config* cfg, const spec_verify_args* a, void* hip_stream);
+
 /* Free the handle.  The caller synchronises the stream first.  NULL is a no-op. */
 int spec_verify_destroy(spec_verify_t* h);
 

@@ -195,3 +195,16 @@ def test_conf_check(B):
     big = B.Config(70000, 2, 1000, B.SV_BF16, 0)
     a = B.make_conf_args(3, 2, conf_logits=fake, temperature=fake, conf_out=fake)
     assert B.conf_check(big, a) == B.SV_EUNSUPPORTED
+
+
+def test_noalloc_rejects_a_call_beyond_its_workspace(B):
+    # 2048 sequences of 16 positions over 129280 tokens need about 30 MB of
+    # workspace, more than the static array: rejected on the host
+    cfg = B.Config(2048, 16, 129280, B.SV_BF16, 0)
+    fake = 1 << 40
+    a = B.make_args(2048, 16, target=fake, draft=fake, tokens=fake, uniforms=fake, temperature=1.0,
+                    target_strides=(17 * 129280, 129280), draft_strides=(16 * 129280, 129280),
+                    accepted_len=fake, out_tokens=fake, verify_len_out=fake)
+    assert B.lib().spec_verify_run_noalloc(ctypes.byref(cfg), ctypes.byref(a), None) == B.SV_EUNSUPPORTED
+    a.B = 9000  # beyond cfg.max_batch: the argument check comes first
+    assert B.lib().spec_verify_run_noalloc(ctypes.byref(cfg), ctypes.byref(a), None) == B.SV_EINVAL
