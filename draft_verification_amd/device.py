@@ -97,17 +97,19 @@ class DeviceProblem:
             self.residual_mass = torch.full((Bn,), nan, **f32)
             self.sampled_prob = torch.full((Bn,), nan, **f32)
 
-    def args(self) -> B.Args:
+    def args(self, counts: bool = True) -> B.Args:
+        """The call's C struct; counts=False leaves out the optional stream
+        counts (rows_read, bytes_read), which cost the step a little work."""
         return B.make_args(
             self.B, self.K, target=self.target, draft=self.draft, tokens=self.tokens, uniforms=self.uniforms,
             temperature=self.temperature, target_strides=self.target_strides, draft_strides=self.draft_strides,
             length_mode=self.length_mode, verify_len=self.verify_len, confidence=self.confidence, tau=self.tau,
             accepted_len=self.accepted_len, out_tokens=self.out_tokens, verify_len_out=self.verify_len_out,
             lse_target=self.lse_target, lse_draft=self.lse_draft, survival=self.survival,
-            residual_mass=self.residual_mass, sampled_prob=self.sampled_prob, rows_read=self.rows_read,
-            device_status=self.device_status, draft_mode=self.draft_mode,
-            target_row_offsets=self.target_row_offsets, draft_row_offsets=self.draft_row_offsets,
-            bytes_read=self.bytes_read)
+            residual_mass=self.residual_mass, sampled_prob=self.sampled_prob,
+            rows_read=self.rows_read if counts else None, device_status=self.device_status,
+            draft_mode=self.draft_mode, target_row_offsets=self.target_row_offsets,
+            draft_row_offsets=self.draft_row_offsets, bytes_read=self.bytes_read if counts else None)
 
     def fetch(self) -> dict:
         torch.cuda.synchronize()
