@@ -82,6 +82,7 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kSplit = 16384;                     // elements per split (fixed for batch invariance)
 constexpr int kPerLane = kSplit / kThreads;       // 64 elements per lane per split
 constexpr int kChunkPos = 32;                     // positions per sv_stream launch
+constexpr int kOpenPolls = 2000;                  // bound on an open walk's wait in sv_stream (about 2 ms)
 
 enum { CTL_STATUS = 0, CTL_DONE = 1, CTL_SCHED_STATUS = 2, CTL_CONF_STATUS = 3, CTL_WORDS = 64 };
 enum { SEQ_BAD = 1, SEQ_OPEN = 2 };               // plan-time flags of a sequence
@@ -1027,10 +1028,28 @@ __global__ __launch_bounds__(kThreads, (DT == SV_BF16 && VEC) ? 8 : 1) void sv_s
     // the sequence's control word as this workgroup starts: dead and lw in one
     // load (a sequence marked bad at plan time has dead = 0), read once and
     // shared so that every wave takes the same decision
-    const unsigned long long cw = control_word(w, b, t);
-    const int dead = (int)(unsigned)cw, L1 = (int)(cw >> 48);
+    unsigned long long cw = control_word(w, b, t);
+    int dead = (int)(unsigned)cw, L1 = (int)(cw >> 48);
     if (!row_needed(p.K, j, draft, dead, L1)) return;
     const int flags = w.seq[b].flags; // set by sv_plan
+    if constexpr (!GREEDY && !OH) {
+        // An open length walk needs the rows of position j >= 2 only if it
+        // passes j - 1 (S_{j-1} >= tau).  Rather than stream them before that
+        // is known, wait until the walk has formed S_{j-1} or closed, or the
+        // sequence was rejected before j: every row the walk waits for was
+        // dispatched earlier and waits for nothing later.  The wait is bounded
+        // (kOpenPolls control-word reads); past it the rows are streamed.
+        if ((flags & SEQ_OPEN) && j >= 2) {
+#pragma clang loop unroll(disable)
+            for (int it = 0; it < kOpenPolls && L1 == 0 && dead >= j && (int)((cw >> 32) & 0xffff) < j - 1; ++it) {
+                __builtin_amdgcn_s_sleep(8);
+                cw = control_word(w, b, t);
+                dead = (int)(unsigned)cw;
+                L1 = (int)(cw >> 48);
+            }
+            if (!row_needed(p.K, j, draft, dead, L1)) return;
+        }
+    }
     int x;
     float u;
     if (stream_row<DT, VEC, GREEDY, MODE>(p, w, b, j, draft, split, flags, L1, redf, redd, redi, t, x, u))
@@ -1400,31 +1419,35 @@ __global__ __launch_bounds__(kThreads) void sv_resid_kernel(Params p, Work w)
     bool bad = false;
 #pragma unroll
     for (int k = 0; k < NL; ++k) {
-        float r[S::RUN], qa[S::RUN], kp[S::RUN], pv[S::RUN];
+        float r[S::RUN], qa[S::RUN];
+        float ks = 0.0f, ps = 0.0f; // kap and P of the run, in token order
 #pragma unroll
         for (int i = 0; i < S::RUN; ++i) {
             bool bi;
-            resid_parts32<DT>(tc.get(k * S::RUN + i), dc.get(k * S::RUN + i), c, r[i], qa[i], kp[i], pv[i], bi);
+            float kk, pv;
+            resid_parts32<DT>(tc.get(k * S::RUN + i), dc.get(k * S::RUN + i), c, r[i], qa[i], kk, pv, bi);
+            ks += kk;
+            ps += pv;
             bad |= bi;
         }
-        // pairwise in fp32 (the residual in the same order as run_mass)
+        // pairwise in fp32 (the residual in the same order as run_mass, which
+        // the draw repeats token by token)
 #pragma unroll
         for (int h = 1; h < S::RUN; h <<= 1)
 #pragma unroll
             for (int i = 0; i + h < S::RUN; i += 2 * h) {
                 r[i] += r[i + h];
                 qa[i] += qa[i + h];
-                kp[i] += kp[i + h];
-                pv[i] += pv[i + h];
             }
-        kap += (double)kp[0];
-        pp += (double)pv[0];
+        kap += (double)ks;
+        pp += (double)ps;
         const double incl = wave_incl_scan((double)r[0], lane);
         const double inclq = wave_incl_scan((double)qa[0], lane);
         if (lane == 63) {
             s_seg[k * kWaves + wv] = incl;
             s_segq[k * kWaves + wv] = inclq;
         }
+        __builtin_amdgcn_sched_barrier(0); // one run at a time (registers)
     }
     const bool anybad = __syncthreads_or(bad);
     kap = block_sum(kap, s_red, t);
