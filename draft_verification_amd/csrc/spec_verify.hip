@@ -84,7 +84,7 @@ constexpr int kPerLane = kSplit / kThreads;       // 64 elements per lane per sp
 constexpr int kChunkPos = 32;                     // positions per sv_stream launch
 constexpr int kOpenPolls = 2000;                  // bound on an open walk's wait in sv_stream (about 2 ms)
 
-enum { CTL_STATUS = 0, CTL_DONE = 1, CTL_SCHED_STATUS = 2, CTL_CONF_STATUS = 3, CTL_WORDS = 64 };
+enum { CTL_SCHED_STATUS = 2, CTL_CONF_STATUS = 3, CTL_WORDS = 64 };
 enum { SEQ_BAD = 1, SEQ_OPEN = 2 };               // plan-time flags of a sequence
 enum { DEC_REJECT = 2, DEC_BAD = 3 };             // decision of a position (written on rejection only)
 // Compile-time variants of the step kernels: MODE_ONEHOT (q is the point mass
@@ -666,10 +666,7 @@ __global__ __launch_bounds__(kThreads) void sv_plan_kernel(Params p, Work w)
     if (r <= K + 1) w.pcnt[pos_index(p, b, r)] = 0; // positions 1 .. K + 1 (R = 2K + 1 >= K + 2)
     if (p.count)
         for (int k = 0; k < p.nsplit; ++k) w.part_m[i * p.nsplit + k] = __uint_as_float(kUnread);
-    if (i == 0) {
-        w.ctl[CTL_STATUS] = 0; // every status bit of this call is raised by sv_draw
-        w.ctl[CTL_DONE] = 0;
-    }
+    if (i == 0 && p.status_out) *p.status_out = 0; // sv_draw raises this call's bits
     if (r != 0) return;
     bool bad = false, open = false;
     int L;
@@ -1191,29 +1188,31 @@ __device__ __forceinline__ float p_mass32(float lt, const DrawCtx& c)
     return scale2(scaled_exp2(lt, c.Mt, c.c_hi, c.c_lo), c.iSt_hi, c.iSt_lo);
 }
 
-// 1 - 2^-D: for |D| < 1/4 from the series of 1 - e^-x (x = D ln 2, to the x^6
-// term: truncation below 4e-8 relative), else 1 - v_exp_f32(-D) (the
-// difference is then at least 0.159, so exp's ulp costs < 4e-7 relative).
+// 1 - 2^-D: for |D| < 1/4 from the series of 1 - e^-x (x = D ln 2) to the x^6
+// term (truncation below 4e-8 relative), written in powers of D, else
+// 1 - v_exp_f32(-D) (the difference is then at least 0.159, so exp's ulp
+// costs < 4e-7 relative).
 __device__ __forceinline__ float one_minus_exp2_neg(float D)
 {
-    const float x = D * 0.693147181f;
-    float s = fmaf(x, -1.0f / 720.0f, 1.0f / 120.0f);
-    s = fmaf(s, x, -1.0f / 24.0f);
-    s = fmaf(s, x, 1.0f / 6.0f);
-    s = fmaf(s, x, -0.5f);
-    s = fmaf(s, x, 1.0f);
-    return fabsf(D) < 0.25f ? s * x : 1.0f - __builtin_amdgcn_exp2f(-D);
+    // the series in D itself: coefficient k is (-1)^(k+1) ln(2)^k / k!
+    float s = fmaf(D, -1.5403530e-4f, 1.3333558e-3f);
+    s = fmaf(s, D, -9.6181291e-3f);
+    s = fmaf(s, D, 5.5504109e-2f);
+    s = fmaf(s, D, -2.4022651e-1f);
+    s = fmaf(s, D, 6.9314718e-1f);
+    return fabsf(D) < 0.25f ? s * D : 1.0f - __builtin_amdgcn_exp2f(-D);
 }
 
 // Residual mass of one token in fp32 (see DrawCtx).  -inf logits: q_v = 0
 // gives D = +inf and r_v = p_v; p_v = 0 gives 0 (a NaN D is dropped by fmaxf).
-template <int DT>
+template <int DT, bool LO = true>
 __device__ __forceinline__ float resid_mass32(float lt, float ld, const DrawCtx& c)
 {
     const float pf = p_mass32(lt, c);
     float u;
     if (DT == SV_BF16) {
-        u = ((lt - ld) - c.dM_hi) - c.dM_lo;
+        u = (lt - ld) - c.dM_hi;
+        if (LO) u -= c.dM_lo;
     } else {
         const float lq = fmaxf(ld, -0x1p127f); // keeps the two-sum finite when q_v = 0
         const float s = lt - lq;
@@ -1225,10 +1224,10 @@ __device__ __forceinline__ float resid_mass32(float lt, float ld, const DrawCtx&
     return pf * fmaxf(one_minus_exp2_neg(D), 0.0f);
 }
 
-template <int DT>
+template <int DT, bool LO = true>
 __device__ __forceinline__ float draw_mass32(float lt, float ld, const DrawCtx& c, bool resid)
 {
-    return resid ? resid_mass32<DT>(lt, ld, c) : p_mass32(lt, c);
+    return resid ? resid_mass32<DT, LO>(lt, ld, c) : p_mass32(lt, c);
 }
 
 // The residual mass of one token with the two sums that renormalise the draft
@@ -1291,26 +1290,41 @@ __device__ __forceinline__ double draw_mass64(float lt, float ld, const DrawCtx&
     return pd * fmax(om, 0.0);
 }
 
-// Inclusive prefix sum over the 64 lanes of a wavefront (fixed order).
-__device__ __forceinline__ double wave_incl_scan(double v, int lane)
+// v of the lane CTRL selects (a DPP row shift or row broadcast), 0 where that
+// lane is out of the row or the row is masked off; both halves of the double.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ double dpp_f64(double v)
 {
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const double n = __shfl_up(v, o);
-        if (lane >= o) v += n;
-    }
+    const long long x = __double_as_longlong(v);
+    const int lo = __builtin_amdgcn_update_dpp(0, (int)x, CTRL, ROWS, 0xf, false);
+    const int hi = __builtin_amdgcn_update_dpp(0, (int)(x >> 32), CTRL, ROWS, 0xf, false);
+    return __longlong_as_double(((long long)hi << 32) | (long long)(unsigned)lo);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wavefront (fixed order): a scan
+// inside each row of 16 lanes (shifts by 1, 2, 4, 8), then row 0's total
+// added to row 1 and row 2's to row 3, then rows 0-1's total to rows 2 and 3.
+// Every kernel that needs lane prefixes calls this, so they agree bit for bit.
+__device__ __forceinline__ double wave_incl_scan(double v, int)
+{
+    v += dpp_f64<0x111, 0xf>(v); // row_shr:1
+    v += dpp_f64<0x112, 0xf>(v); // row_shr:2
+    v += dpp_f64<0x114, 0xf>(v); // row_shr:4
+    v += dpp_f64<0x118, 0xf>(v); // row_shr:8
+    v += dpp_f64<0x142, 0xa>(v); // row_bcast:15 into rows 1 and 3
+    v += dpp_f64<0x143, 0xc>(v); // row_bcast:31 into rows 2 and 3
     return v;
 }
 
 // Mass of a run of RUN consecutive tokens: per-token fp32 masses summed
 // pairwise in fp32 (at most 3 roundings deep), then widened.  Every kernel
 // that needs a run's mass calls this, so the sums agree bit for bit.
-template <int DT, int RUN>
+template <int DT, int RUN, bool LO = true>
 __device__ __forceinline__ double run_mass(const float (&lt)[RUN], const float (&ld)[RUN], const DrawCtx& c, bool resid)
 {
     float m[RUN];
 #pragma unroll
-    for (int i = 0; i < RUN; ++i) m[i] = draw_mass32<DT>(lt[i], ld[i], c, resid);
+    for (int i = 0; i < RUN; ++i) m[i] = draw_mass32<DT, LO>(lt[i], ld[i], c, resid);
 #pragma unroll
     for (int w = 1; w < RUN; w <<= 1)
 #pragma unroll
@@ -1399,17 +1413,34 @@ __global__ __launch_bounds__(kThreads) void sv_resid_kernel(Params p, Work w)
     dc.template load<VEC>(seq_row<DT, PK>(p.d, p.doff, p.dbs, p.drs, b, f.js - 1), split * kSplit, p.V, t, q);
     const long long so = ((long long)b * p.nsplit + split) * kSegStride + q * QSEG;
     if (!fine) {
+        // bf16 maxima differ exactly in fp32 (the low part of Mt - Md is then
+        // 0 and subtracting it changes no bit): one instruction less per token
+        if (DT == SV_BF16 && c.dM_lo == 0.0f) {
 #pragma unroll
-        for (int k = 0; k < NL; ++k) {
-            float lt[S::RUN], ld[S::RUN];
+            for (int k = 0; k < NL; ++k) {
+                float lt[S::RUN], ld[S::RUN];
 #pragma unroll
-            for (int i = 0; i < S::RUN; ++i) {
-                lt[i] = tc.get(k * S::RUN + i);
-                ld[i] = dc.get(k * S::RUN + i);
+                for (int i = 0; i < S::RUN; ++i) {
+                    lt[i] = tc.get(k * S::RUN + i);
+                    ld[i] = dc.get(k * S::RUN + i);
+                }
+                const double r = run_mass<DT, S::RUN, false>(lt, ld, c, true);
+                const double incl = wave_incl_scan(r, lane);
+                if (lane == 63) s_seg[k * kWaves + wv] = incl;
             }
-            const double r = run_mass<DT, S::RUN>(lt, ld, c, true);
-            const double incl = wave_incl_scan(r, lane);
-            if (lane == 63) s_seg[k * kWaves + wv] = incl;
+        } else {
+#pragma unroll
+            for (int k = 0; k < NL; ++k) {
+                float lt[S::RUN], ld[S::RUN];
+#pragma unroll
+                for (int i = 0; i < S::RUN; ++i) {
+                    lt[i] = tc.get(k * S::RUN + i);
+                    ld[i] = dc.get(k * S::RUN + i);
+                }
+                const double r = run_mass<DT, S::RUN>(lt, ld, c, true);
+                const double incl = wave_incl_scan(r, lane);
+                if (lane == 63) s_seg[k * kWaves + wv] = incl;
+            }
         }
         __syncthreads();
         if (t < QSEG) w.seg[so + t] = s_seg[t];
@@ -1777,16 +1808,7 @@ __global__ __launch_bounds__(kThreads) void sv_draw_kernel(Params p, Work w)
         if (p.pys) p.pys[b] = py;
         int bits = 0;
         if (kind == KIND_BAD) bits |= (f.L < 0 && !(w.seq[b].flags & SEQ_BAD)) ? SV_STATUS_INCOMPLETE : SV_STATUS_BAD_INPUT;
-        if (p.status_out) {
-            // every workgroup raises its bits, then counts itself done; the
-            // last one reads the call's word and clears it for the next call
-            if (bits) or_status(&w.ctl[CTL_STATUS], bits);
-            stores_done();
-            if (add_ag(&w.ctl[CTL_DONE], 1) == p.B - 1) {
-                *p.status_out = ld_ag(&w.ctl[CTL_STATUS]);
-                st_ag(&w.ctl[CTL_STATUS], 0);
-            }
-        }
+        if (bits && p.status_out) or_status(p.status_out, bits);
     }
 }
 
