@@ -1548,6 +1548,17 @@ __global__ __launch_bounds__(kThreads) void sv_draw_kernel(Params p, Work w)
     // drafted tokens this thread copies to the output
     const float uf32 = (p.u == nullptr) ? 0.0f : p.u[(long long)b * (K + 1) + K];
     const int tok0 = tid < K ? p.tok[(long long)b * K + tid] : -1;
+    // the segment sums a replacement draw needs, requested before the state is
+    // known (one value per thread at V = 129280; unused for other draws)
+    constexpr int kSegPre = 2;
+    double segv[kSegPre];
+    const double* sg = w.seg + (long long)b * p.nsplit * kSegStride;
+    const int nseg = GREEDY || OH ? 0 : p.nsplit * S::SEGS;
+#pragma unroll
+    for (int k = 0; k < kSegPre; ++k) {
+        const int i = tid + k * kThreads;
+        segv[k] = i < nseg ? sg[(i / S::SEGS) * kSegStride + i % S::SEGS] : 0.0;
+    }
     const Final f = final_state(p, w, b, GREEDY);
     int kind = f.kind;
     const int a = f.a;
@@ -1565,10 +1576,12 @@ __global__ __launch_bounds__(kThreads) void sv_draw_kernel(Params p, Work w)
         if (kind == KIND_RESID && !OH) {
             Md = w.row_m[rb + K + js];
             Sd = w.row_s[rb + K + js];
-            // every segment sum of the sequence at once (one round trip): the
-            // split totals and the search inside the chosen split both read LDS
-            const double* sg = w.seg + (long long)b * p.nsplit * kSegStride;
-            for (int i = tid; i < p.nsplit * S::SEGS; i += kThreads)
+            // every segment sum of the sequence in LDS: the split totals and
+            // the search inside the chosen split both read them
+#pragma unroll
+            for (int k = 0; k < kSegPre; ++k)
+                if (tid + k * kThreads < nseg) s_all[tid + k * kThreads] = segv[k];
+            for (int i = tid + kSegPre * kThreads; i < nseg; i += kThreads)
                 s_all[i] = sg[(i / S::SEGS) * kSegStride + i % S::SEGS];
             __syncthreads();
         }
