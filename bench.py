@@ -523,15 +523,25 @@ def time_packed(torch, B, D, synth, steps, warmup, pw):
         prob = synth.make_problem(base.with_(seed=3 + s))
         prob.verify_len = L.astype(np.int32)
         probs.append(prob)
-    for layout in ("packed", "dense"):
-        dps = [D.packed_from_problem(p, L, diagnostics=False) if layout == "packed"
+    # the engine knows its lengths once it has built the verify batch: every
+    # call but "packed_no_bound" passes their maximum as max_verify_len
+    out["max_verify_len"] = int(L.max())
+    for layout in ("packed", "dense", "packed_no_bound"):
+        dps = [D.packed_from_problem(p, L, diagnostics=False) if layout != "dense"
                else D.from_problem(p, diagnostics=False) for p in probs]
+        for d in dps:
+            d.max_verify_len = 0 if layout == "packed_no_bound" else int(L.max())
         sv = B.SpecVerify(Bn, K, base.V, base.dtype, 0)
         argv = [d.args(counts=False) for d in dps]
         ms = time_block(torch, sv, argv, steps, warmup, pw)
         kt = kernel_times(torch, sv, argv, steps, pw)
         outs = count_pass(torch, sv, dps)
         sv.close()
+        if layout == "packed_no_bound":
+            out[layout] = {"ms_per_step": ms, "kernel_avg_ms": kt}
+            del dps, argv, outs
+            torch.cuda.empty_cache()
+            continue
         bc = [byte_counts(o, p) for o, p in zip(outs, probs)]
         needed = sum(c["needed"] for c in bc) / 2.0
         streamed = sum(c["streamed"] for c in bc) / 2.0

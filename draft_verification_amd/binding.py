@@ -51,7 +51,7 @@ class Args(ctypes.Structure):
         ("residual_mass", ctypes.c_void_p), ("sampled_prob", ctypes.c_void_p), ("rows_read", ctypes.c_void_p),
         ("device_status", ctypes.c_void_p), ("draft_mode", ctypes.c_int32),
         ("target_row_offsets", ctypes.c_void_p), ("draft_row_offsets", ctypes.c_void_p),
-        ("bytes_read", ctypes.c_void_p),
+        ("bytes_read", ctypes.c_void_p), ("max_verify_len", ctypes.c_int32),
     ]
 
 
@@ -146,7 +146,7 @@ def make_args(B: int, K: int, *, target, draft=None, tokens, uniforms=None, temp
               accepted_len, out_tokens, verify_len_out, lse_target=None, lse_draft=None, survival=None,
               residual_mass=None, sampled_prob=None, rows_read=None, device_status=None,
               draft_mode: int = SV_DRAFT_PROBS, target_row_offsets=None, draft_row_offsets=None,
-              bytes_read=None) -> Args:
+              bytes_read=None, max_verify_len: int = 0) -> Args:
     """Fill an Args struct.  Strides are (batch, row) in elements."""
     return Args(
         B, K, _addr(target), int(target_strides[0]), int(target_strides[1]),
@@ -156,7 +156,7 @@ def make_args(B: int, K: int, *, target, draft=None, tokens, uniforms=None, temp
         _addr(accepted_len), _addr(out_tokens), _addr(verify_len_out),
         _addr(lse_target), _addr(lse_draft), _addr(survival), _addr(residual_mass), _addr(sampled_prob),
         _addr(rows_read), _addr(device_status), int(draft_mode), _addr(target_row_offsets),
-        _addr(draft_row_offsets), _addr(bytes_read))
+        _addr(draft_row_offsets), _addr(bytes_read), int(max_verify_len))
 
 
 def check(cfg: Config, args: Args) -> int:

@@ -149,6 +149,7 @@ struct Params {
     const long long* toff;     // packed rows: target rows of sequence b start at row toff[b] (NULL: dense)
     const long long* doff;     // packed rows: draft rows of sequence b start at row doff[b]
     int len_mode;
+    int lbound;                // fixed lengths: every L_b <= lbound (0: no bound); positions past lbound + 1 are not launched
     const void* t;
     long long tbs, trs;
     const void* d;
@@ -676,9 +677,10 @@ __global__ __launch_bounds__(kThreads) void sv_plan_kernel(Params p, Work w)
         L = (int)(nt - 1);
         if (nt < 1 || nt > K + 1) bad = true;
         if (p.doff && p.doff[b + 1] - p.doff[b] != nt - 1) bad = true;
+        if (p.lbound && L > p.lbound) bad = true; // its later rows are not launched
     } else if (p.len_mode == SV_LEN_FIXED) {
         L = p.vl_in ? p.vl_in[b] : K;
-        if (L < 0 || L > K) bad = true;
+        if (L < 0 || L > K || (p.lbound && L > p.lbound)) bad = true;
     } else if (p.conf) {
         // given confidences: S_j = S_{j-1} c_j, L = max({0} U {j : S_j >= tau})
         const double tau = (double)p.tau[b];
@@ -700,8 +702,10 @@ __global__ __launch_bounds__(kThreads) void sv_plan_kernel(Params p, Work w)
             for (int j = 0; j < K; ++j) p.surv[(long long)b * K + j] = 1.0f;
     }
     SeqCtl c;
-    c.dead = bad ? 0 : K + 2; // a bad sequence needs no row
-    c.lw = (bad || open) ? 0 : ((L + 1) << 16);
+    // a bad sequence needs no row: dead = 0 and a closed length (L + 1 = 1),
+    // since an unknown length would ask for every draft row
+    c.dead = bad ? 0 : K + 2;
+    c.lw = bad ? (1 << 16) : (open ? 0 : ((L + 1) << 16));
     c.flags = (bad ? SEQ_BAD : 0) | (open ? SEQ_OPEN : 0);
     c.Lout = L;
     w.seq[b] = c;
@@ -2148,8 +2152,10 @@ void enqueue_step(const Params& p, const Work& w, hipStream_t s, Launch& launch)
     const unsigned B = (unsigned)p.B, ns = (unsigned)p.nsplit;
     const unsigned long long R = 2ull * p.K + 1;
     launch(K_PLAN, sv_plan_kernel, dim3((unsigned)((B * R + kThreads - 1) / kThreads)), 0, p, w);
-    for (int j0 = 1; j0 <= p.K + 1; j0 += kChunkPos) {
-        const unsigned np = (unsigned)std::min(kChunkPos, p.K + 2 - j0);
+    // positions 1 .. Lmax + 1: a bounded call's later positions need no row
+    const int Lmax = p.lbound ? p.lbound : p.K;
+    for (int j0 = 1; j0 <= Lmax + 1; j0 += kChunkPos) {
+        const unsigned np = (unsigned)std::min(kChunkPos, Lmax + 2 - j0);
         launch(K_STREAM, sv_stream_kernel<DT, VEC, GR, MODE>, dim3(np * B * SLOTS * ns), 0, p, w, j0);
     }
     if constexpr (!GR && !OH)
@@ -2216,6 +2222,7 @@ Params make_params(const spec_verify_config* cfg, const spec_verify_args* a)
     p.nsplit = nsplit_of(cfg->vocab);
     p.greedy = greedy;
     p.len_mode = a->length_mode;
+    p.lbound = a->max_verify_len;
     p.derived = (a->length_mode == SV_LEN_TAU && !a->confidence) ? 1 : 0;
     p.onehot = (!greedy && a->draft_mode == SV_DRAFT_ONEHOT) ? 1 : 0;
     p.count = (a->rows_read || a->bytes_read) ? 1 : 0;
@@ -2330,6 +2337,8 @@ int spec_verify_check(const spec_verify_config* cfg, const spec_verify_args* a)
     const float T = a->temperature;
     if (!(T >= 0.0f) || isinf(T)) return SV_EINVAL;
     if (a->length_mode != SV_LEN_FIXED && a->length_mode != SV_LEN_TAU) return SV_EINVAL;
+    if (a->max_verify_len < 0 || a->max_verify_len > a->K) return SV_EINVAL;
+    if (a->max_verify_len && a->length_mode != SV_LEN_FIXED) return SV_EINVAL;
     if (a->B == 0) return SV_OK;
     const int V = cfg->vocab;
     if (!a->target_logits || a->target_row_stride < V || a->target_batch_stride < 0) return SV_EINVAL;

@@ -56,6 +56,7 @@ class DeviceProblem:
     draft_mode: int = B.SV_DRAFT_PROBS
     target_row_offsets: Optional[torch.Tensor] = None  # packed rows: [B+1] int64
     draft_row_offsets: Optional[torch.Tensor] = None
+    max_verify_len: int = 0  # fixed lengths: the caller's bound on every L_b (0: none)
 
     @staticmethod
     def upload(target: np.ndarray, draft: Optional[np.ndarray], tokens: np.ndarray,
@@ -109,7 +110,8 @@ class DeviceProblem:
             residual_mass=self.residual_mass, sampled_prob=self.sampled_prob,
             rows_read=self.rows_read if counts else None, device_status=self.device_status,
             draft_mode=self.draft_mode, target_row_offsets=self.target_row_offsets,
-            draft_row_offsets=self.draft_row_offsets, bytes_read=self.bytes_read if counts else None)
+            draft_row_offsets=self.draft_row_offsets, bytes_read=self.bytes_read if counts else None,
+            max_verify_len=self.max_verify_len)
 
     def fetch(self) -> dict:
         torch.cuda.synchronize()

@@ -167,6 +167,15 @@ typedef struct {
                                       a different count marks the sequence bad).  Required with
                                       target_row_offsets when T > 0 and SV_DRAFT_PROBS. */
     int64_t* bytes_read;           /* optional [B] */
+    int32_t max_verify_len;        /* 0 = no bound.  SV_LEN_FIXED only (dense or packed), 1..K: the
+                                      caller's promise that every L_b <= max_verify_len, as an
+                                      engine knows once it has built the verify batch (the packed
+                                      layout's row counts, or admission's lengths).  The step then
+                                      launches no work for positions past max_verify_len + 1, so
+                                      short verify batches do not pay for K + 1 positions.  A
+                                      sequence whose L_b exceeds the bound is marked bad (a = 0, no
+                                      token, SV_STATUS_BAD_INPUT); the others' outputs are those
+                                      of the unbounded call, bit for bit. */
 } spec_verify_args;
 
 /* Allocate a handle and its workspace on cfg->device.  *out is set only on SV_OK. */

@@ -70,6 +70,7 @@ def test_check_accepts_valid_arguments(B):
     ("temperature", float("inf")), ("length_mode", 7), ("target_logits", None), ("draft_tokens", None),
     ("target_row_stride", 999), ("target_batch_stride", -1), ("draft_logits", None), ("uniforms", None),
     ("draft_row_stride", 10), ("accepted_len", None), ("out_tokens", None), ("verify_len_out", None),
+    ("max_verify_len", -1), ("max_verify_len", 5),
 ])
 def test_check_rejects(B, field, value):
     cfg, a = _valid(B)
@@ -87,6 +88,16 @@ def test_greedy_needs_no_draft_but_tau_needs_a_confidence(B):
     a.confidence = 1 << 40
     assert B.check(cfg, a) == B.SV_OK
     a.tau = None
+    assert B.check(cfg, a) == B.SV_EINVAL
+
+
+def test_length_bound_is_for_fixed_lengths_only(B):
+    cfg, a = _valid(B)
+    for bound in (1, 4):
+        a.max_verify_len = bound
+        assert B.check(cfg, a) == B.SV_OK
+    cfg, a = _valid(B, mode=B.SV_LEN_TAU)
+    a.max_verify_len = 2
     assert B.check(cfg, a) == B.SV_EINVAL
 
 

@@ -166,6 +166,8 @@ def test_bad_tokens_and_lengths_set_status():
     assert res["device_status"][0] & 1
     for b in (1, 2, 4, 5):
         assert res["accepted_len"][b] == 0 and np.all(res["out_tokens"][b] == -1)
+    for b in (4, 5):    # marked bad before any row: none is read
+        assert res["rows_read"][b] == 0 and res["bytes_read"][b] == 0, b
     assert res["accepted_len"][3] == 2
 
 

@@ -98,8 +98,76 @@ def test_bad_row_counts():
     for b in range(w.B):
         if b in bad:
             assert res["accepted_len"][b] == 0 and (res["out_tokens"][b] == -1).all(), b
+            assert res["rows_read"][b] == 0 and res["bytes_read"][b] == 0, b
     good = [b for b in range(w.B) if b not in bad]
     prob.verify_len = np.clip(L, 0, w.K).astype(np.int32)
     orc = O.verify_problem(prob, seqs=good, all_rows=True)
     rep = PU.compare("packed bad counts", res, orc, dtype=w.dtype, prob=prob)
     assert not rep.mismatches, rep.mismatches[:5]
+
+
+def _bounded(dp, bound):
+    dp.max_verify_len = int(bound)
+    return dp
+
+
+@pytest.mark.parametrize("layout", ["dense", "packed"])
+def test_length_bound_changes_nothing_but_the_launch(layout):
+    """With max_verify_len = max L_b the step launches positions 1 .. max L_b + 1
+    only; its outputs (diagnostics included) equal the unbounded call's bit for
+    bit, and its stream counts stay within the needed rows and the window."""
+    D = _D()
+    w = BASE.with_(K=8, seed=87)
+    L = np.random.default_rng(87).integers(0, 4, size=w.B).astype(np.int32)
+    L[:2] = [0, 3]
+    prob = synth.make_problem(w)
+    prob.verify_len = L
+    make = (lambda: D.packed_from_problem(prob, L)) if layout == "packed" else (lambda: D.from_problem(prob))
+    print(f"[case] bound {layout} B={w.B} K={w.K} V={w.V} max L={L.max()}", flush=True)
+    free = D.run_once(make())
+    for bound in (int(L.max()), int(L.max()) + 2, w.K):
+        res = D.run_once(_bounded(make(), bound))
+        assert not PU.same_outputs(res, free), bound
+        assert not PU.check_streamed(res, w.K, w.V, 2, two_rows=True), bound
+    assert int(free["device_status"][0]) == 0
+
+
+@pytest.mark.parametrize("layout", ["dense", "packed"])
+def test_length_bound_marks_longer_sequences_bad(layout):
+    """A sequence whose L_b exceeds max_verify_len is marked bad (a = 0, no
+    token, status bit) and none of its rows is read; the others match the
+    oracle."""
+    D = _D()
+    w = BASE.with_(B=12, K=5, V=7000, seed=88)
+    L = np.array([0, 1, 2, 3, 4, 5, 2, 1, 5, 0, 3, 2], np.int32)
+    bound = 2
+    prob = synth.make_problem(w)
+    prob.verify_len = L
+    dp = D.packed_from_problem(prob, L) if layout == "packed" else D.from_problem(prob)
+    print(f"[case] bound {bound} marks bad, {layout}", flush=True)
+    res = D.run_once(_bounded(dp, bound))
+    assert int(res["device_status"][0]) == 1
+    bad = [b for b in range(w.B) if L[b] > bound]
+    for b in bad:
+        assert res["accepted_len"][b] == 0 and (res["out_tokens"][b] == -1).all(), b
+        assert res["rows_read"][b] == 0 and res["bytes_read"][b] == 0, b
+    good = [b for b in range(w.B) if L[b] <= bound]
+    orc = O.verify_problem(prob, seqs=good, all_rows=True)
+    rep = PU.compare(f"bound {layout}", res, orc, dtype=w.dtype, prob=prob)
+    print(rep.line(), flush=True)
+    assert not rep.mismatches, rep.mismatches[:5]
+
+
+def test_length_bound_full_size_admission_lengths():
+    """The full-size shape with admission-like lengths (mostly 0 .. 4) and the
+    bound at their maximum, packed: equal to the unbounded dense call."""
+    D = _D()
+    w = synth.WORKLOADS["sched256"].with_(length_mode=synth.LEN_FIXED, tau_choices=())
+    L = np.minimum(np.random.default_rng(89).geometric(0.55, size=w.B) - 1, w.K).astype(np.int32)
+    prob = synth.make_problem(w)
+    prob.verify_len = L
+    print(f"[case] bound full size max L={L.max()} sum L={L.sum()}", flush=True)
+    dense = D.run_once(D.from_problem(prob))
+    res = D.run_once(_bounded(D.packed_from_problem(prob, L), int(L.max())))
+    assert not PU.same_outputs(res, dense)
+    assert int(res["device_status"][0]) == 0
