@@ -100,12 +100,18 @@ constexpr unsigned kUnread = 0x7fbadbadu;         // part_m bits of a split no w
 // lowered with atomic min.  lw: (L + 1) << 16 |
 // f, where L + 1 == 0 while the verify length is still open and f is the number
 // of survivals S_1..S_f the open walk has formed; moved with compare-and-swap.
+// Each sequence's word has a 128-byte line to itself (every workgroup of the
+// step reads its word with a coherent load, and the decisions update it with
+// atomics): with 16-byte words eight sequences shared a line, and sv_stream
+// took 40.3 us instead of 37.2 at B = 64, K = 8.
 struct SeqCtl {
     int dead;
     int lw;
     int flags;  // SEQ_*
     int Lout;   // verify length as given (reported for a sequence marked bad)
+    int pad[28];
 };
+static_assert(sizeof(SeqCtl) == 128, "one control word per 128-byte line");
 
 struct Work {
     int* ctl;
@@ -701,14 +707,13 @@ __global__ __launch_bounds__(kThreads) void sv_plan_kernel(Params p, Work w)
         if (p.onehot && p.surv)
             for (int j = 0; j < K; ++j) p.surv[(long long)b * K + j] = 1.0f;
     }
-    SeqCtl c;
     // a bad sequence needs no row: dead = 0 and a closed length (L + 1 = 1),
     // since an unknown length would ask for every draft row
-    c.dead = bad ? 0 : K + 2;
-    c.lw = bad ? (1 << 16) : (open ? 0 : ((L + 1) << 16));
-    c.flags = (bad ? SEQ_BAD : 0) | (open ? SEQ_OPEN : 0);
-    c.Lout = L;
-    w.seq[b] = c;
+    SeqCtl* c = &w.seq[b];
+    c->dead = bad ? 0 : K + 2;
+    c->lw = bad ? (1 << 16) : (open ? 0 : ((L + 1) << 16));
+    c->flags = (bad ? SEQ_BAD : 0) | (open ? SEQ_OPEN : 0);
+    c->Lout = L;
 }
 
 // ---------------------------------------------------------------- sv_stream
@@ -1071,7 +1076,7 @@ struct Final {
 
 __device__ __forceinline__ Final final_state(const Params& p, const Work& w, int b, bool greedy)
 {
-    const SeqCtl c = w.seq[b];
+    const SeqCtl& c = w.seq[b];
     const int K = p.K;
     Final f;
     f.y = -1;

@@ -193,3 +193,57 @@ def test_chi_square_shared_rows(mode):
         counts = np.bincount(res["out_tokens"][sel, j], minlength=V)
         pv = stats.chisquare(counts, p[j] * sel.sum()).pvalue
         assert pv > 1e-4, (j, pv)
+
+
+def test_one_handle_across_call_kinds():
+    """A handle's step state (control words, counters, stream marks) is zero
+    between steps: calls of every kind and shape in a row on one handle give
+    the outputs of the same calls on fresh handles, bit for bit (stream counts
+    within their bounds)."""
+    D = _D()
+    from draft_verification_amd import binding as B
+    V, Bmax, Kmax = 20000, 24, 8
+    peaked = synth.WORKLOADS["peaked512"].with_(B=Bmax, K=Kmax, V=V, dtype=synth.BF16, seed=301)
+    cases = []
+    # fixed lengths, counted
+    p0 = synth.make_problem(synth.WORKLOADS["zipf64"].with_(B=Bmax, K=Kmax, V=V, seed=302))
+    cases.append(("fixed counted", lambda: D.from_problem(p0), True))
+    # open length walks (derived confidences), not counted
+    p1 = synth.make_problem(peaked.with_(tau_choices=(0.05, 0.3, 0.6)))
+    cases.append(("open walks", lambda: D.from_problem(p1), False))
+    # given confidences, a smaller batch and block
+    p2 = synth.make_problem(peaked.with_(B=9, K=5, length_mode=synth.LEN_TAU, tau_choices=(0.0, 0.3, 0.7)))
+    p2.confidence = (np.random.default_rng(303).random((9, 5)) ** 0.3).astype(np.float32)
+    cases.append(("given confidences", lambda: D.from_problem(p2), True))
+    # greedy
+    p3 = synth.make_problem(synth.WORKLOADS["greedy1024"].with_(B=Bmax, K=Kmax, V=V, seed=304))
+    cases.append(("greedy", lambda: D.from_problem(p3), True))
+    # packed rows with bad counts and a length bound
+    p4 = synth.make_problem(synth.WORKLOADS["zipf64"].with_(B=12, K=Kmax, V=V, seed=305))
+    L4 = np.array([0, 3, 9, 2, 1, -1, 4, 4, 2, 0, 6, 3], np.int64)
+
+    def packed():
+        dp = D.packed_from_problem(p4, L4)
+        dp.max_verify_len = 5
+        return dp
+    cases.append(("packed, bad counts", packed, True))
+    # bad lengths in the dense layout, then the first call again
+    p5 = synth.make_problem(synth.WORKLOADS["zipf64"].with_(B=Bmax, K=Kmax, V=V, seed=306))
+    p5.verify_len = np.array([8, -2, 3, 9, 0] + [5] * (Bmax - 5), np.int32)
+    cases.append(("bad lengths", lambda: D.from_problem(p5), True))
+    cases.append(("fixed counted again", lambda: D.from_problem(p0), True))
+
+    sv = B.SpecVerify(Bmax, Kmax, V, synth.BF16, 0)
+    for name, make, counts in cases:
+        print(f"[case] one handle: {name}", flush=True)
+        dp = make()
+        sv.run(dp.args(counts=counts))
+        got = dp.fetch()
+        ref = D.run_once(make())
+        assert not PU.same_outputs(got, ref), name
+        np.testing.assert_array_equal(got["device_status"], ref["device_status"])
+        if counts:
+            assert not PU.check_streamed(got, dp.K, V, 2, two_rows=name != "greedy"), name
+            for b in np.flatnonzero(got["out_tokens"][:, 0] < 0):  # marked bad: no row read
+                assert got["rows_read"][b] == 0, (name, b)
+    sv.close()
