@@ -1132,8 +1132,9 @@ struct Seg {
 };
 constexpr int kSegStride = 64; // segment sums stored per split
 
-// Token masses of the final draw.  p_v = 2^((l_v - Mt) c) / St with 1/St in two
-// fp32 parts (~2^-48 relative); a replacement takes r_v = max(0, p_v - q_v) as
+// Token masses of the final draw.  p_v = 2^((l_v - Mt) c) / St: per token in
+// fp32 without the 1/St, which scales each run's fp32 sum once it is widened
+// to fp64; a replacement takes r_v = max(0, p_v - q_v) as
 // p_v (1 - 2^-D_v) with D_v = log2(p_v / q_v) = c ((lt_v - ld_v) - (Mt - Md)) +
 // log2(Sd / St): the logit difference is exact (a two-sum for fp32 logits;
 // bf16 logits differ exactly in fp32), Mt - Md and log2(Sd / St) come from fp64
@@ -1141,12 +1142,11 @@ constexpr int kSegStride = 64; // segment sums stored per split
 // keeps its relative accuracy when p and q nearly agree (no cancellation of
 // two separately rounded masses).
 struct DrawCtx {
-    float Mt, c_hi, c_lo, iSt_hi, iSt_lo;
+    float Mt, c_hi, c_lo;
     float dM_hi, dM_lo, k_hi, k_lo, c32;
     double Mt64, iSt64, dM64, k64, c64;
 };
 
-__device__ __forceinline__ float scale2(float e, float hi, float lo) { return fmaf(e, hi, e * lo); }
 
 __device__ __forceinline__ DrawCtx make_ctx(float Mt, double St, float Md, double Sd, bool resid, const Params& p)
 {
@@ -1154,8 +1154,6 @@ __device__ __forceinline__ DrawCtx make_ctx(float Mt, double St, float Md, doubl
     c.Mt = Mt;
     c.Mt64 = (double)Mt;
     c.iSt64 = 1.0 / St;
-    c.iSt_hi = (float)c.iSt64;
-    c.iSt_lo = (float)(c.iSt64 - (double)c.iSt_hi);
     c.c_hi = p.c_hi;
     c.c_lo = p.c_lo;
     c.c32 = p.c32;
@@ -1184,7 +1182,6 @@ __device__ __forceinline__ DrawCtx uniform_ctx(const DrawCtx& c)
 {
     DrawCtx u;
     u.Mt = uniform_f32(c.Mt); u.c_hi = uniform_f32(c.c_hi); u.c_lo = uniform_f32(c.c_lo);
-    u.iSt_hi = uniform_f32(c.iSt_hi); u.iSt_lo = uniform_f32(c.iSt_lo);
     u.dM_hi = uniform_f32(c.dM_hi); u.dM_lo = uniform_f32(c.dM_lo);
     u.k_hi = uniform_f32(c.k_hi); u.k_lo = uniform_f32(c.k_lo); u.c32 = uniform_f32(c.c32);
     u.Mt64 = uniform_f64(c.Mt64); u.iSt64 = uniform_f64(c.iSt64); u.dM64 = uniform_f64(c.dM64);
@@ -1192,9 +1189,10 @@ __device__ __forceinline__ DrawCtx uniform_ctx(const DrawCtx& c)
     return u;
 }
 
+// St p_v in fp32 (the target mass before the 1/St).
 __device__ __forceinline__ float p_mass32(float lt, const DrawCtx& c)
 {
-    return scale2(scaled_exp2(lt, c.Mt, c.c_hi, c.c_lo), c.iSt_hi, c.iSt_lo);
+    return scaled_exp2(lt, c.Mt, c.c_hi, c.c_lo);
 }
 
 // 1 - 2^-D: for |D| < 1/4 from the series of 1 - e^-x (x = D ln 2) to the x^6
@@ -1212,7 +1210,7 @@ __device__ __forceinline__ float one_minus_exp2_neg(float D)
     return fabsf(D) < 0.25f ? s * D : 1.0f - __builtin_amdgcn_exp2f(-D);
 }
 
-// Residual mass of one token in fp32 (see DrawCtx).  -inf logits: q_v = 0
+// Residual mass of one token in fp32, times St (see DrawCtx).  -inf logits: q_v = 0
 // gives D = +inf and r_v = p_v; p_v = 0 gives 0 (a NaN D is dropped by fmaxf).
 template <int DT, bool LO = true>
 __device__ __forceinline__ float resid_mass32(float lt, float ld, const DrawCtx& c)
@@ -1240,7 +1238,8 @@ __device__ __forceinline__ float draw_mass32(float lt, float ld, const DrawCtx& 
 }
 
 // The residual mass of one token with the two sums that renormalise the draft
-// row against the target row (see the renormalisation at sv_draw): qa = q_v
+// row against the target row (see the renormalisation at sv_draw), all times
+// St: qa = q_v
 // on the residual's support (where p > q) and kap = p_v - q_v (signed, over
 // every token), both as p_v times a factor of 2^-D.  bad: the token's q_v
 // exceeds p_v by more than 2^120 (a target logit of -inf where the draft has
@@ -1325,9 +1324,10 @@ __device__ __forceinline__ double wave_incl_scan(double v, int)
     return v;
 }
 
-// Mass of a run of RUN consecutive tokens: per-token fp32 masses summed
-// pairwise in fp32 (at most 3 roundings deep), then widened.  Every kernel
-// that needs a run's mass calls this, so the sums agree bit for bit.
+// Mass of a run of RUN consecutive tokens: per-token fp32 masses (times St)
+// summed pairwise in fp32 (at most 3 roundings deep), then widened and scaled
+// by 1/St.  Every kernel that needs a run's mass calls this, so the sums agree
+// bit for bit.
 template <int DT, int RUN, bool LO = true>
 __device__ __forceinline__ double run_mass(const float (&lt)[RUN], const float (&ld)[RUN], const DrawCtx& c, bool resid)
 {
@@ -1338,7 +1338,7 @@ __device__ __forceinline__ double run_mass(const float (&lt)[RUN], const float (
     for (int w = 1; w < RUN; w <<= 1)
 #pragma unroll
         for (int i = 0; i + w < RUN; i += 2 * w) m[i] += m[i + w];
-    return (double)m[0];
+    return (double)m[0] * c.iSt64;
 }
 
 // Segment sums of one split (all 256 threads): lane run sums of RUN tokens,
@@ -1479,10 +1479,10 @@ __global__ __launch_bounds__(kThreads) void sv_resid_kernel(Params p, Work w)
                 r[i] += r[i + h];
                 qa[i] += qa[i + h];
             }
-        kap += (double)ks;
-        pp += (double)ps;
-        const double incl = wave_incl_scan((double)r[0], lane);
-        const double inclq = wave_incl_scan((double)qa[0], lane);
+        kap += (double)ks * c.iSt64;
+        pp += (double)ps * c.iSt64;
+        const double incl = wave_incl_scan((double)r[0] * c.iSt64, lane);
+        const double inclq = wave_incl_scan((double)qa[0] * c.iSt64, lane);
         if (lane == 63) {
             s_seg[k * kWaves + wv] = incl;
             s_segq[k * kWaves + wv] = inclq;
@@ -1721,7 +1721,8 @@ __global__ __launch_bounds__(kThreads) void sv_draw_kernel(Params p, Work w)
 #pragma unroll
                 for (int i = 0; i < S::RUN; ++i) resid_parts32<DT>(lt[i], ld[i], c, rr[i], qq[i], kk, pp, bb);
 #pragma unroll
-                for (int i = 0; i < S::RUN; ++i) m[i] = fmax((double)rr[i] - F1 * (double)qq[i], 0.0);
+                for (int i = 0; i < S::RUN; ++i)
+                    m[i] = fmax((double)rr[i] * c.iSt64 - F1 * ((double)qq[i] * c.iSt64), 0.0);
 #pragma unroll
                 for (int h = 1; h < S::RUN; h <<= 1)
 #pragma unroll
@@ -1729,11 +1730,11 @@ __global__ __launch_bounds__(kThreads) void sv_draw_kernel(Params p, Work w)
                         rr[i] += rr[i + h];
                         qq[i] += qq[i + h];
                     }
-                r = fmax((double)rr[0] - F1 * (double)qq[0], 0.0);
+                r = fmax((double)rr[0] * c.iSt64 - F1 * ((double)qq[0] * c.iSt64), 0.0);
             } else {
                 r = run_mass<DT, S::RUN>(lt, ld, c, resid);
 #pragma unroll
-                for (int i = 0; i < S::RUN; ++i) m[i] = (double)draw_mass32<DT>(lt[i], ld[i], c, resid);
+                for (int i = 0; i < S::RUN; ++i) m[i] = (double)draw_mass32<DT>(lt[i], ld[i], c, resid) * c.iSt64;
             }
 #pragma unroll
             for (int i = 0; i < S::RUN; ++i)
