@@ -44,8 +44,9 @@
 // and loads (coherent across the chip's eight L2 caches) and arrival counters:
 // a writer waits for its stores to complete before the atomic that hands them
 // over, so no L2 write-back fence is needed (that fence costs ~130 ns per
-// workgroup, serialised).  No workgroup ever waits for another: a workgroup
-// that is not last at a counter simply exits.
+// workgroup, serialised).  A workgroup that is not last at a counter simply
+// exits; the only wait is that of a workgroup of an open length walk for the
+// walk to reach its position, a bounded poll of rows dispatched before it.
 //
 // Numerics.  bf16 and fp32 inputs are exact in fp32.  The row statistics take
 // one fma per element, l*c - round(m*c) with c = log2(e)/T in fp32, and keep
