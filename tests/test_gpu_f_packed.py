@@ -111,24 +111,33 @@ def _bounded(dp, bound):
     return dp
 
 
-@pytest.mark.parametrize("layout", ["dense", "packed"])
-def test_length_bound_changes_nothing_but_the_launch(layout):
+@pytest.mark.parametrize("layout,mode", [("dense", "probs"), ("packed", "probs"), ("dense", "greedy"),
+                                         ("packed", "onehot"), ("dense", "fp32")])
+def test_length_bound_changes_nothing_but_the_launch(layout, mode):
     """With max_verify_len = max L_b the step launches positions 1 .. max L_b + 1
     only; its outputs (diagnostics included) equal the unbounded call's bit for
-    bit, and its stream counts stay within the needed rows and the window."""
+    bit, and its stream counts stay within the needed rows and the window
+    (draft probabilities, greedy and one-hot drafts, bf16 and fp32)."""
     D = _D()
     w = BASE.with_(K=8, seed=87)
+    if mode == "greedy":
+        w = w.with_(temperature=0.0)
+    elif mode == "onehot":
+        w = w.with_(draft_mode=1, token_mode=2)
+    elif mode == "fp32":
+        w = w.with_(dtype=synth.F32)
     L = np.random.default_rng(87).integers(0, 4, size=w.B).astype(np.int32)
     L[:2] = [0, 3]
     prob = synth.make_problem(w)
     prob.verify_len = L
     make = (lambda: D.packed_from_problem(prob, L)) if layout == "packed" else (lambda: D.from_problem(prob))
-    print(f"[case] bound {layout} B={w.B} K={w.K} V={w.V} max L={L.max()}", flush=True)
+    print(f"[case] bound {layout} {mode} B={w.B} K={w.K} V={w.V} max L={L.max()}", flush=True)
     free = D.run_once(make())
+    es = 4 if w.dtype == synth.F32 else 2
     for bound in (int(L.max()), int(L.max()) + 2, w.K):
         res = D.run_once(_bounded(make(), bound))
         assert not PU.same_outputs(res, free), bound
-        assert not PU.check_streamed(res, w.K, w.V, 2, two_rows=True), bound
+        assert not PU.check_streamed(res, w.K, w.V, es, two_rows=mode in ("probs", "fp32")), bound
     assert int(free["device_status"][0]) == 0
 
 
