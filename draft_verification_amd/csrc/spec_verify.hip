@@ -1139,9 +1139,9 @@ constexpr int kSegStride = 64; // segment sums stored per split
 // p_v (1 - 2^-D_v) with D_v = log2(p_v / q_v) = c ((lt_v - ld_v) - (Mt - Md)) +
 // log2(Sd / St): the logit difference is exact (a two-sum for fp32 logits;
 // bf16 logits differ exactly in fp32), Mt - Md and log2(Sd / St) come from fp64
-// in two fp32 parts, and 1 - 2^-D comes from its series when |D| < 1/4, so r_v
-// keeps its relative accuracy when p and q nearly agree (no cancellation of
-// two separately rounded masses).
+// in two fp32 parts, and 1 - 2^-D comes from a polynomial in D when |D| < 1/4
+// (one_minus_exp2_neg), so r_v keeps its relative accuracy when p and q nearly
+// agree (no cancellation of two separately rounded masses).
 struct DrawCtx {
     float Mt, c_hi, c_lo;
     float dM_hi, dM_lo, k_hi, k_lo, c32;
